@@ -1,0 +1,304 @@
+"""Benchmark of one DeepSeek-R1-style MoE layer on one MI355X.
+
+A step is one pass of the whole layer through the C ABI -- moe_route,
+moe_permute, moe_expert_ffn_gate_up, moe_expert_ffn_down, moe_combine -- over
+one batch of synthetic tokens already resident in HBM. The default workload
+is the R1 decode layer in bf16: 256 tokens, hidden 7168, 256 routed experts
+(intermediate 2048, top-8 by sigmoid score with Zipf(1.1)-skewed popularity)
+plus one shared expert. Other workloads (--config 3, 4, 5) are available for
+measurement; only the default run is the headline line.
+
+Printed: one JSON line with tokens/s, the roofline of the dominant kernel
+(the gate/up grouped GEMM: algorithmic bytes per launch over its average
+duration, timed with HIP events on the launch stream inside the timed
+region) and the CPU oracle's throughput on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU + % of HBM/MFMA roofline (R1-shaped)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--cpu-sample", type=int, default=16,
+                    help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
+    return ap.parse_args()
+
+
+def build_layer(cid: int, dev: str):
+    import torch
+    import moe_inputs as mi
+    import mixture_experts_layer_select_amd as L
+
+    cfg = mi.CONFIGS[cid]
+    info = {}
+    topk = None
+    if cid == 3:
+        ids, w, recv = mi.ep_share_routing(cfg, device=dev)
+        x = mi.ep_share_tokens(cfg, len(recv), device=dev)
+        st = mi.stacked_expert_weights(cfg, range(cfg.E_local), device=dev)
+        layer = L.MoELayer(cfg.fmt, cfg.H, cfg.I, cfg.k, st["w13"], st["w2"], st["w13_scale"],
+                           st["w2_scale"], shared=None, router=None)
+        topk = (ids, w)
+        info["T_recv"] = len(recv)
+        return cfg, layer, x, st, None, topk, info
+    if cid == 5:
+        return build_partition_layer(cfg, dev)
+    st = mi.stacked_expert_weights(cfg, range(cfg.E), device=dev)
+    sh = mi.shared_weights(cfg, device=dev) if cfg.shared else None
+    router = dict(w=mi.router_weight(cfg, device=dev), bias=mi.router_bias(cfg, device=dev),
+                  scoring=L.SIGMOID, renormalize=True)
+    layer = L.MoELayer(cfg.fmt, cfg.H, cfg.I, cfg.k, st["w13"], st["w2"], st["w13_scale"],
+                       st["w2_scale"], shared=sh, router=router)
+    x = mi.tokens(cfg, device=dev)
+    return cfg, layer, x, st, sh, topk, info
+
+
+def build_partition_layer(cfg, dev):
+    """Calibrate expert counts, partition 256 experts into 8 balanced sets of
+    32, remap the router, and build the heaviest set's layer."""
+    import numpy as np
+    import torch
+    import moe_inputs as mi
+    import mixture_experts_layer_select_amd as L
+
+    G = cfg.extra["groups"]
+    S = cfg.E // G
+    wr = mi.router_weight(cfg, device=dev)
+    bias = mi.router_bias(cfg, device=dev)
+
+    def counts_of(x, w, b):
+        T = x.shape[0]
+        logits = torch.empty((T, cfg.E), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+        L.moe_route(x, w, b, L.BF16, T, cfg.H, cfg.E, cfg.k, L.SIGMOID, True, logits, ids, tw)
+        cnt = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+        off = torch.empty(cfg.E + 2, dtype=torch.int32, device=dev)
+        r2s = torch.empty(T * cfg.k + T, dtype=torch.int32, device=dev)
+        s2r = torch.empty(T * cfg.k, dtype=torch.int32, device=dev)
+        n = L.moe_permute_workspace_size(T, cfg.k, cfg.E)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        L.moe_permute(ids, T, cfg.k, 0, cfg.E, False, None, L.BF16, 0, L.BF16, cnt, off, r2s, s2r,
+                      None, None, ws, n)
+        return cnt[: cfg.E].cpu().to(torch.int64), ids, tw
+
+    xc = mi.calibration_tokens(cfg, device=dev)
+    counts, _, _ = counts_of(xc, wr, bias)
+    n2o = torch.empty(cfg.E, dtype=torch.int32)
+    o2n = torch.empty(cfg.E, dtype=torch.int32)
+    loads = torch.empty(G, dtype=torch.int64)
+    L.moe_balanced_partition(counts, cfg.E, G, n2o, o2n, loads)
+    contiguous = counts.view(G, S).sum(1)
+    mean = counts.sum().item() / G
+    # remap the router rows and bias into the new expert order
+    n2o_d = n2o.to(dev)
+    wr2 = torch.empty_like(wr)
+    L.moe_gather_rows(wr, cfg.E, wr2, n2o_d, cfg.E, cfg.H * 2)
+    b2 = torch.empty_like(bias)
+    L.moe_gather_rows(bias, cfg.E, b2, n2o_d, cfg.E, 4)
+    x = mi.tokens(cfg, device=dev)
+    ev_before, _, _ = counts_of(x, wr, bias)
+    ev_after, ids, tw = counts_of(x, wr2, b2)
+    g_before = ev_before.view(G, S).sum(1)
+    g_after = ev_after.view(G, S).sum(1)
+    heavy = int(torch.argmax(g_after).item())
+    heavy_before = int(torch.argmax(g_before).item())
+    old_ids = n2o[heavy * S:(heavy + 1) * S].tolist()
+    st = mi.stacked_expert_weights(cfg, old_ids, device=dev)
+    layer = L.MoELayer(cfg.fmt, cfg.H, cfg.I, cfg.k, st["w13"], st["w2"], shared=None, router=None,
+                       expert_base=heavy * S)
+    info = dict(
+        calib_max_over_mean_contiguous=round(contiguous.max().item() / mean, 4),
+        calib_max_over_mean_balanced=round(loads.max().item() / mean, 4),
+        eval_max_over_mean_contiguous=round(g_before.max().item() / (ev_before.sum().item() / G), 4),
+        eval_max_over_mean_balanced=round(g_after.max().item() / (ev_after.sum().item() / G), 4),
+        heaviest_group=heavy, heaviest_group_rows=int(g_after.max().item()),
+        heaviest_group_rows_contiguous=int(g_before.max().item()),
+        heaviest_group_hit_experts=int((ev_after.view(G, S)[heavy] > 0).sum().item()),
+    )
+    return cfg, layer, x, st, None, (ids, tw), info
+
+
+def alg_bytes_gate_up(cfg, layer, counts, n_rows):
+    """Algorithmic bytes of one gate/up launch: the w13 panels of every group
+    with rows (once), the permuted activations read once, A written once."""
+    wb = 1 if cfg.fmt == "fp8" else 2
+    hit = int((counts[: layer.E_local] > 0).sum()) + (1 if layer.shared is not None else 0)
+    w13 = 2 * cfg.I * cfg.H * wb + (2 * cfg.I // 128) * (cfg.H // 128) * 4 * (cfg.fmt == "fp8")
+    xin = n_rows * cfg.H * wb + (n_rows * cfg.H // 128 * 4 if cfg.fmt == "fp8" else 0)
+    aout = n_rows * cfg.I * wb + (n_rows * cfg.I // 128 * 4 if cfg.fmt == "fp8" else 0)
+    return hit * w13 + xin + aout, hit
+
+
+def layer_alg(cfg, layer, counts, T, n_rows):
+    """Whole-layer algorithmic bytes and flops: weights (+scales) of the hit
+    experts and the shared expert, router rows, x read once, out written once,
+    routing ids/weights; flops 2*(2I*H + H*I) per routed or shared row."""
+    wb = 1 if cfg.fmt == "fp8" else 2
+    hit = int((counts[: layer.E_local] > 0).sum()) + (1 if layer.shared is not None else 0)
+    per_expert = 3 * cfg.I * cfg.H * wb
+    if cfg.fmt == "fp8":
+        per_expert += ((2 * cfg.I // 128) * (cfg.H // 128) + (cfg.H // 128) * (cfg.I // 128)) * 4
+    router = layer.router["w"].numel() * 2 if layer.router is not None else 0
+    byt = hit * per_expert + router + 2 * T * cfg.H * 2 + T * cfg.k * 8
+    flops = 2.0 * 3 * cfg.I * cfg.H * n_rows
+    return byt, flops
+
+
+def cpu_groups(st, sh, ids, base, E_local):
+    """Host copies of the experts that the sampled tokens pick (+ shared)."""
+    used = sorted({int(e) - base for e in ids.ravel() if 0 <= int(e) - base < E_local})
+    groups = [None] * E_local
+    for e in used:
+        d = dict(w13=st["w13"][e].cpu(), w2=st["w2"][e].cpu())
+        if st.get("w13_scale") is not None:
+            d["w13_scale"] = st["w13_scale"][e].cpu()
+            d["w2_scale"] = st["w2_scale"][e].cpu()
+        groups[e] = d
+    shared = None if sh is None else {k: (v.cpu() if v is not None else None) for k, v in sh.items()}
+    return groups, shared
+
+
+def cpu_baseline(cfg, layer, b, x, st, sh, topk, n_sample):
+    """The oracle as it stands on a bounded sample: gating of every token of
+    the batch (when the layer has a router) plus the rest of the layer for
+    n_sample tokens; the per-token cost is scaled to tokens/s."""
+    import numpy as np
+    import torch
+    import oracle
+
+    T = x.shape[0]
+    xc = x.cpu()
+    t_route = 0.0
+    if layer.router is not None:
+        wr = layer.router["w"].cpu()
+        bias = layer.router["bias"].cpu() if layer.router["bias"] is not None else None
+        t0 = time.perf_counter()
+        _, ids, w = oracle.route(xc, wr, bias, cfg.k, oracle.SIGMOID, True)
+        t_route = time.perf_counter() - t0
+    else:
+        ids, w = topk[0].cpu().numpy(), topk[1].cpu().numpy()
+    rows = np.sort(np.random.default_rng(0).choice(T, min(n_sample, T), replace=False))
+    groups, shared = cpu_groups(st, sh, ids[rows], layer.expert_base, layer.E_local)
+    t0 = time.perf_counter()
+    oracle.moe_layer(xc[torch.from_numpy(rows)], cfg.k, groups, shared, topk_ids=ids[rows],
+                     topk_w=w[rows], base=layer.expert_base, E_local=layer.E_local,
+                     fmt=oracle.FP8 if cfg.fmt == "fp8" else None)
+    t_rest = time.perf_counter() - t0
+    per_token = t_route / T + t_rest / len(rows)
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
+    return {"value": round(1.0 / per_token, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"gating of all {T} tokens ({t_route:.2f} s) + permute/FFN/combine of "
+                      f"{len(rows)} seeded tokens ({t_rest:.2f} s), fp64 FFN, scaled per token"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer runs on one "
+              "GPU's share and uses no collectives.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import mixture_experts_layer_select_amd as L
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] building workload config {args.config}")
+    cfg, layer, x, st, sh, topk, info = build_layer(args.config, dev)
+    T = x.shape[0]
+    b = layer.buffers(T, dev)
+    cap = T * cfg.k + T
+    stream = torch.cuda.current_stream()
+    ids_in, w_in = (topk if topk is not None else (None, None))
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        if ids_in is None:
+            layer.route(x, b)
+        layer.permute(x, b, ids_in)
+        if i is not None:
+            ev[i][0].record(stream)
+        L.moe_expert_ffn_gate_up(layer.weights, b.x_perm, b.x_perm_scale, b.offsets, layer.n_groups,
+                                 cap, b.ws_ffn, b.ws_ffn.numel())
+        if i is not None:
+            ev[i][1].record(stream)
+        L.moe_expert_ffn_down(layer.weights, b.offsets, layer.n_groups, cap, b.y_perm, b.ws_ffn,
+                              b.ws_ffn.numel())
+        layer.combine(b, w_in)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    tokens = T
+    value = tokens / (ms / 1e3)
+    k_ms = float(np.mean([a.elapsed_time(z) for a, z in ev]))
+
+    counts = b.counts.cpu().numpy()
+    n_rows = int(b.offsets[-1].item())
+    gbytes, hit = alg_bytes_gate_up(cfg, layer, counts, n_rows)
+    achieved = gbytes / (k_ms / 1e3) / 1e9
+    lbytes, lflops = layer_alg(cfg, layer, counts, T, n_rows)
+    fmt_key = "fp8" if cfg.fmt == "fp8" else "bf16"
+    t_roof = max(lbytes / (HBM_PEAK_GBS * 1e9), lflops / (MFMA_PEAK_TFLOPS[fmt_key] * 1e12))
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "f32": "f32"}[cfg.fmt], "data": "synthetic",
+        "config": {"workload": f"c{cfg.cid} {cfg.name}", "tokens": T, "hidden": cfg.H,
+                   "experts": cfg.E, "local_experts": layer.E_local, "top_k": cfg.k,
+                   "intermediate": cfg.I, "shared_expert": layer.shared is not None,
+                   "experts_hit": hit - (1 if layer.shared is not None else 0),
+                   "rows": n_rows, **info},
+        "roofline": {"kernel": f"ffn_gemm_{fmt_key}_kernel<gate_up>", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(gbytes), "avg_launch_ms": round(k_ms, 4)},
+        "layer_roofline": {"bytes": int(lbytes), "flops": lflops,
+                           "t_roof_ms": round(t_roof * 1e3, 4),
+                           "frac": round(t_roof * 1e3 / ms, 4),
+                           "hbm_GBs": round(lbytes / (ms / 1e3) / 1e9, 1),
+                           "tflops": round(lflops / (ms / 1e3) / 1e12, 2)},
+        "cpu_baseline": None,
+    }
+    if args.cpu_sample > 0:
+        log(f"[bench] cpu oracle baseline on {args.cpu_sample} tokens")
+        line["cpu_baseline"] = cpu_baseline(cfg, layer, b, x, st, sh, topk, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

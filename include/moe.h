@@ -1,0 +1,198 @@
+/*
+ * moe.h -- C ABI of libmoe.so: one DeepSeek-R1-style mixture-of-experts layer
+ * on one MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The layer, as the sources state it:
+ *   [Moreh-EP]   Moreh, "DeepSeek inference at 21K output tokens/s on AMD
+ *                Instinct MI300X GPUs with expert parallelism":
+ *                Overview (a lightweight gating network picks a few experts
+ *                per token), Parallelization (R1: 256 routed experts, 8 active
+ *                per token, one always-on shared expert; 32 experts per GPU at
+ *                EP=8), Inter-GPU load balancing (activation counts, balanced
+ *                sets of 32, remapped gating), Library optimization (fused MoE
+ *                kernel; horizontal fusion of the shared expert's GEMMs),
+ *                HIP Graphs (tensor sizes kept static for graph capture).
+ *   [SGLang-H20] "Deploying DeepSeek-R1 efficiently on H20-96G together with
+ *                SGLang": Prefill solutions (MoE fp8 b_scale handling, down
+ *                projection input layout), SwapAB GEMM (variable M per expert
+ *                needs small M tiles).
+ *
+ * Conventions shared by every call:
+ *  - All tensors are caller-allocated device memory, row-major, densely
+ *    packed. The library never allocates or frees device memory; scratch
+ *    space is a caller-provided workspace whose size a *_workspace_size query
+ *    returns.
+ *  - Device calls only enqueue work on `stream` (a hipStream_t, NULL = the
+ *    default stream): no host synchronisation, no device-to-host copies, so a
+ *    sequence of calls can be captured into a HIP graph. Per-expert row counts
+ *    stay on the device; buffers are sized by the static bound T*k (+T).
+ *  - bf16 is IEEE bfloat16; fp8 is OCP e4m3fn (max 448). Expert weights are
+ *    K-contiguous: w13 [E][2I][H] with rows 0..I-1 the gate projection and
+ *    I..2I-1 the up projection, w2 [E][H][I]. fp8 weights carry one fp32
+ *    scale per 128x128 block ([E][2I/128][H/128], [E][H/128][I/128]); fp8
+ *    activations one fp32 scale per 1x128 block of a row.
+ *  - Errors are reported synchronously by the return value; argument checks
+ *    happen before anything is enqueued. Faults inside kernels surface at the
+ *    caller's next synchronisation. Data values (NaN/Inf) are not checked.
+ *  - T == 0 is a successful no-op.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1  /* null pointer, negative size, k > E, ...      */
+#define MOE_ERR_UNSUPPORTED 2  /* a size or dtype combination not built       */
+#define MOE_ERR_HIP 3          /* a HIP runtime call or kernel launch failed  */
+#define MOE_ERR_WORKSPACE 4    /* workspace null or smaller than required     */
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_scoring;
+
+/* Gating ([Moreh-EP] Overview, Parallelization; remapped order after the
+ * load balancer, Inter-GPU load balancing).
+ *   logits[t,e] = sum_h x[t,h] * w_router[e,h] (+ bias[e])
+ * accumulated in fp32 in a fixed order (64 partial sums; partial j takes the
+ * 8-element chunks h with floor(h/8) mod 64 == j in ascending h with fused
+ * multiply-adds from +0; partials combined p[j] += p[j+s] for s = 32..1; then
+ * one add of the bias), so the result is reproducible bit for bit.
+ * topk_ids[t,:] = the k experts with the largest logits, ordered by (logit
+ * descending, expert index ascending). topk_w = softmax or sigmoid of the
+ * picked logits, renormalised to sum 1 over the k picks when `renormalize`
+ * (softmax without it is normalised over all E).
+ *   x [T,H], w_router [E,H]: dt = MOE_F32 or MOE_BF16 (both the same dt)
+ *   bias [E] fp32 or NULL; logits [T,E] fp32 (out); topk_ids [T,k] int32 (out);
+ *   topk_w [T,k] fp32 (out).
+ * Limits: 1 <= k <= E <= 256 (MOE_ERR_UNSUPPORTED above), H >= 1. */
+moe_status moe_route(const void* x, const void* w_router, const float* bias, moe_dtype dt,
+                     int T, int H, int E, int k, moe_scoring scoring, int renormalize,
+                     float* logits, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Token -> expert grouping ([Moreh-EP] Library optimization: the fused MoE
+ * kernel consumes tokens grouped per expert; Inter-GPU load balancing: the
+ * per-expert activation counts). Slots s = t*k + j whose id lies in
+ * [expert_base, expert_base + E_local) are local; they become rows ordered by
+ * (expert, slot). Group E_local is the shared expert ([Moreh-EP]
+ * Parallelization: runs on every token): with include_shared it holds the T
+ * tokens in order after the routed rows.
+ *   expert_counts [E_local+1] (out), expert_offsets [E_local+2] (out,
+ *   exclusive scan of the counts; R = offsets[E_local] routed rows),
+ *   row_to_slot [T*k+T] (out; shared rows hold T*k+t, unused rows -1),
+ *   slot_to_row [T*k] (out; -1 = not local),
+ *   x_perm [T*k+T, H] (out): x[token(row)] as a bit copy (perm_dt == x_dt)
+ *   or, for perm_dt = MOE_FP8_E4M3 with bf16 x, e4m3 codes with
+ *   x_perm_scale [T*k+T, H/128] fp32 (out): per 1x128 block s = amax/448 (1 for
+ *   an all-zero block), code = e4m3(clamp(v/s, +-448)), fp32 division, round to
+ *   nearest even. x and x_perm may both be NULL (maps and counts only).
+ * ids outside the local range (including negative ones) are simply not local.
+ * Limits: 1 <= E_local <= 256; T*k+T < 2^31; fp8 needs H % 128 == 0.
+ * workspace: moe_permute_workspace_size(T, k, E_local) bytes. */
+size_t moe_permute_workspace_size(int T, int k, int E_local);
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int expert_base, int E_local,
+                       int include_shared, const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_to_slot,
+                       int32_t* slot_to_row, void* x_perm, float* x_perm_scale,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* Expert weights of one GPU's share: E_local routed experts plus an optional
+ * shared expert (ws13/ws2, NULL when there is none), all in `dt`. The scale
+ * pointers are used for MOE_FP8_E4M3 only. For MOE_F32 and MOE_BF16 the
+ * activations are in the same dt; for MOE_FP8_E4M3 they are e4m3 + scales. */
+typedef struct moe_expert_weights {
+    moe_dtype dt;
+    int E_local, H, I;
+    const void* w13;
+    const float* w13_scale;
+    const void* w2;
+    const float* w2_scale;
+    const void* ws13;
+    const float* ws13_scale;
+    const void* ws2;
+    const float* ws2_scale;
+} moe_expert_weights;
+
+/* Expert FFNs as grouped GEMMs with a device-resident, variable row count
+ * per group ([SGLang-H20] SwapAB GEMM: variable M per expert; [Moreh-EP]
+ * Library optimization: the shared expert joins the same launch, horizontal
+ * fusion). For the rows of group g (rows [offsets[g], offsets[g+1])):
+ *   [G|U] = x_perm w13_g^T,  A = silu(G) * U,  y_perm = A w2_g^T
+ * groups 0..E_local-1 use the routed experts, group E_local (n_groups ==
+ * E_local+1) the shared expert. fp32 accumulation. bf16: A is rounded to bf16
+ * between the GEMMs. fp8: A is quantised per 1x128 block exactly like x_perm
+ * (fp32 scale amax/448, round to nearest even), and block scales are applied
+ * to each 128-deep partial product.
+ *   x_perm [max_rows, H] (+ x_perm_scale [max_rows, H/128] for fp8),
+ *   expert_offsets [n_groups+1] (device; as written by moe_permute),
+ *   y_perm [max_rows, H] (out): bf16 (fp32 for dt = MOE_F32).
+ * max_rows bounds offsets[n_groups] (T*k+T for the maps of moe_permute).
+ * Limits: bf16 needs H % 128 == 0 and I % 128 == 0; fp8 needs H % 256 == 0
+ * and I % 128 == 0; E_local <= 1024; n_groups in {E_local, E_local+1} (the
+ * latter needs the shared weights).
+ * workspace: moe_expert_ffn_workspace_size(w, max_rows) bytes. */
+size_t moe_expert_ffn_workspace_size(const moe_expert_weights* w, int max_rows);
+moe_status moe_expert_ffn(const moe_expert_weights* w, const void* x_perm,
+                          const float* x_perm_scale, const int32_t* expert_offsets, int n_groups,
+                          int max_rows, void* y_perm, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/* moe_expert_ffn as its two steps, one kernel each, for callers that time or
+ * schedule them separately. gate_up computes A = silu(x_perm w13^T gate) *
+ * (x_perm w13^T up) into the workspace (bf16, or e4m3 + 1x128 scales);
+ * down reads A from the same workspace (written by the preceding gate_up on
+ * the same stream with the same offsets) and writes y_perm. Arguments,
+ * limits and workspace size as for moe_expert_ffn. */
+moe_status moe_expert_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
+                                  const float* x_perm_scale, const int32_t* expert_offsets,
+                                  int n_groups, int max_rows, void* workspace, size_t ws_bytes,
+                                  void* stream);
+moe_status moe_expert_ffn_down(const moe_expert_weights* w, const int32_t* expert_offsets,
+                               int n_groups, int max_rows, void* y_perm, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Routing-weighted combine back to token order ([Moreh-EP] Overview:
+ * dispatch/combine; the local half of it).
+ *   out[t] = sum_{j: slot_to_row[t*k+j] >= 0} topk_w[t,j] * y_perm[slot_to_row[t*k+j]]
+ *            + y_perm[expert_offsets[shared_group] + t]   (if shared_group >= 0)
+ * summed in fp32 in slot order, then rounded to nearest even.
+ *   y_perm [.., H] in y_dt (MOE_BF16 or MOE_F32), out [T,H] in out_dt
+ *   (MOE_BF16 or MOE_F32). */
+moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* slot_to_row,
+                       const float* topk_w, int T, int k, int H, const int32_t* expert_offsets,
+                       int shared_group, void* out, moe_dtype out_dt, void* stream);
+
+/* Host-only balanced partition of E experts into G sets of E/G with balanced
+ * activation totals ([Moreh-EP] Inter-GPU load balancing: a balanced number
+ * partitioning variant). LPT under the set-size limit (experts by count
+ * descending, id ascending, each to the least-loaded non-full set, lower set
+ * on ties), then best-improvement swaps out of the heaviest set (the swap of
+ * a in the heaviest set g* with b in set h that minimises max(L_g* - d,
+ * L_h + d) < L_g*, d = c_a - c_b > 0; ties to the smallest h, a, b) until no
+ * swap improves (at most 10*E swaps). All pointers are host memory:
+ * counts [E] (>= 0), new_to_old [E] (out; set g is new ids g*E/G.., old ids
+ * ascending), old_to_new [E] (out), group_loads [G] (out). */
+moe_status moe_balanced_partition(const int64_t* counts, int E, int G, int32_t* new_to_old,
+                                  int32_t* old_to_new, int64_t* group_loads);
+
+/* Gather whole rows: dst[i] = src[index[i]] for i < n_rows, each row
+ * row_bytes long (a multiple of 4). Applies the balanced partition's expert
+ * order to router rows, router bias and expert weights ([Moreh-EP]
+ * Inter-GPU load balancing: reorder the experts, remap the gating).
+ * index [n_rows] int32 is device memory with values in [0, n_src_rows). */
+moe_status moe_gather_rows(const void* src, int n_src_rows, void* dst, const int32_t* index,
+                           int n_rows, size_t row_bytes, void* stream);
+
+const char* moe_status_string(moe_status s);
+/* detail of the last error on the calling thread ("" if none) */
+const char* moe_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

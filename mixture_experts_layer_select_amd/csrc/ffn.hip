@@ -1,0 +1,572 @@
+// Expert FFNs as grouped GEMMs with a device-resident row count per group
+// ([SGLang-H20] SwapAB GEMM: the per-expert M varies from token to token, so
+// tiles must stay small in M; [Moreh-EP] Library optimization: fused MoE
+// kernel, and the shared expert's GEMMs joined into the same launch).
+//
+// Work decomposition. expert_offsets (device) define m-tiles of <= 64 rows
+// per group; a persistent grid walks the (m-tile, n-block) work items; every item streams one panel of expert weight
+// rows over the full K exactly once, so in the memory-bound decode regime
+// each hit expert's weights cross HBM once per 64 rows.
+//
+// Inside a work item (4 wavefronts): the 64 x 128 activation tile of each
+// K step is staged in LDS (double buffered) and shared by the 4 waves; each
+// wave streams its own weight rows straight from HBM into registers, one K
+// step ahead of the MFMAs, with 64-byte contiguous pieces per lane. MFMA
+// operands take the weights as A (16 rows of N) and the activations as B
+// (16 rows of M); a group's rows are padded with zeros to the next multiple
+// of 16 and m-subtiles past the group's rows are skipped, so a sparsely hit
+// expert costs one 16-row MFMA side, not a fixed 64.
+//
+// The lane -> K assignment of the loaded pieces is a permutation of the K
+// step; A and B use the same one, so the dot products are unchanged.
+//
+// bf16: v_mfma_f32_16x16x32_bf16, 4 per K step of 128 per (n, m) subtile.
+// fp8:  v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales, one per K
+//       step of 128 = one 128x128 weight block and one 1x128 activation
+//       block; the fp32 block scales multiply each partial product.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 64;      // rows per m-tile
+constexpr int kBK = 128;     // K per step
+constexpr int kThreads = 256;
+
+// m-tiles: group g's rows [offsets[g], offsets[g+1]) split into tiles of
+// kBM rows; tiles are numbered group after group. Every workgroup builds the
+// exclusive prefix of tiles per group in LDS once (n_groups <= 1025) and
+// maps a work item to (group, first row, rows) by binary search. Rows at or
+// past max_rows are dropped, so inconsistent offsets cannot push a row index
+// outside the caller's buffers.
+constexpr int kMaxGroups = 1025;
+
+struct MTile {
+    int group, row0, rows;
+};
+
+__device__ __forceinline__ int clamp_row(int r, int max_rows) {
+    return r < 0 ? 0 : (r > max_rows ? max_rows : r);
+}
+
+struct TileMap {
+    int start[kMaxGroups + 1];  // start[g] = first tile of group g; start[n_groups] = total
+    int part[256];
+};
+
+// all threads of the block must call; returns the total number of tiles
+__device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int n_groups,
+                              int max_rows) {
+    const int per = (n_groups + 255) / 256;
+    const int g0 = threadIdx.x * per;
+    int local[5];  // per <= 5 since n_groups <= 1025 (+ slack)
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int g = g0 + i;
+        int nt = 0;
+        if (i < per && g < n_groups) {
+            const int m = clamp_row(offsets[g + 1], max_rows) - clamp_row(offsets[g], max_rows);
+            nt = m > 0 ? (m + kBM - 1) / kBM : 0;
+        }
+        local[i] = nt;
+        sum += nt;
+    }
+    tm.part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
+        const int v = threadIdx.x >= off ? tm.part[threadIdx.x - off] : 0;
+        __syncthreads();
+        tm.part[threadIdx.x] += v;
+        __syncthreads();
+    }
+    int run = tm.part[threadIdx.x] - sum;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int g = g0 + i;
+        if (i < per && g < n_groups) tm.start[g] = run;
+        run += local[i];
+    }
+    if (threadIdx.x == 255) tm.start[n_groups] = tm.part[255];
+    __syncthreads();
+    return tm.start[n_groups];
+}
+
+__device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __restrict__ offsets,
+                                         int n_groups, int max_rows, int mt) {
+    int lo = 0, hi = n_groups - 1;  // last g with start[g] <= mt
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tm.start[mid] <= mt) lo = mid;
+        else hi = mid - 1;
+    }
+    MTile t;
+    t.group = lo;
+    const int r0 = clamp_row(offsets[lo], max_rows);
+    const int r1 = clamp_row(offsets[lo + 1], max_rows);
+    t.row0 = r0 + (mt - tm.start[lo]) * kBM;
+    t.rows = min(kBM, r1 - t.row0);
+    return t;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    // format 0 = e4m3 for both operands; E8M0 scale 127 = 1.0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// ============================================================================ bf16
+// SwiGLU (GEMM-1): W = w13 [G][2I][K=H]; an item covers 64 intermediate columns:
+//   wave w owns gate rows n0+16w.. and up rows I+n0+16w.. (n0 = nb*64)
+//   out = A [rows][I] bf16 = silu(gate) * up
+// Down (GEMM-2): W = w2 [G][H][K=I]; an item covers 128 output columns:
+//   wave w owns rows n0+32w.. and n0+32w+16.. (n0 = nb*128); out = y [rows][H]
+constexpr int kLdsRowBf16 = kBK * 2 + 16;  // bytes per staged activation row (16 B pad)
+
+template <bool kSwiGLU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void ffn_gemm_bf16_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ws,
+    int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
+    int NB, uint16_t* __restrict__ out, int ldo) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kBM * kLdsRowBf16];
+    __shared__ TileMap tm;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;   // row of the 16x? operand piece
+    const int lk = lane >> 4;   // which 32-wide K quarter of the step
+    const int nk = K / kBK;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows) * NB;
+
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB);
+        const int nb = item % NB;
+        const uint16_t* Wg =
+            tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
+        int ra, rb;
+        if (kSwiGLU) {
+            ra = nb * 64 + 16 * wave + li;
+            rb = ra + Nw / 2;
+        } else {
+            ra = nb * 128 + 32 * wave + li;
+            rb = ra + 16;
+        }
+        const uint16_t* wa = Wg + (size_t)ra * K + 32 * lk;
+        const uint16_t* wb = Wg + (size_t)rb * K + 32 * lk;
+        const int nms = (tile.rows + 15) >> 4;
+
+        // activation staging: thread -> (row tr, 32-element quarter tq)
+        const int tr = threadIdx.x >> 2, tq = threadIdx.x & 3;
+        const bool xin = tr < tile.rows;
+        const uint16_t* xsrc = X + (size_t)(tile.row0 + (xin ? tr : 0)) * K + 32 * tq;
+
+        f32x4 acc_a[4], acc_b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc_a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc_b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        u32x4 wa_cur[4], wb_cur[4], wa_nxt[4], wb_nxt[4], xr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wa_cur[i] = reinterpret_cast<const u32x4*>(wa)[i];
+            wb_cur[i] = reinterpret_cast<const u32x4*>(wb)[i];
+            xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc)[i] : u32x4{0, 0, 0, 0};
+        }
+        {
+            u32x4* d = reinterpret_cast<u32x4*>(&xs[0][tr * kLdsRowBf16 + 64 * tq]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] = xr[i];
+        }
+        __syncthreads();
+
+        for (int kc = 0; kc < nk; ++kc) {
+            const int buf = kc & 1;
+            const bool more = kc + 1 < nk;
+            if (more) {
+                const int ko = (kc + 1) * kBK;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    wa_nxt[i] = reinterpret_cast<const u32x4*>(wa + ko)[i];
+                    wb_nxt[i] = reinterpret_cast<const u32x4*>(wb + ko)[i];
+                    xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc + ko)[i] : u32x4{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                if (ms < nms) {
+                    const u32x4* bp = reinterpret_cast<const u32x4*>(
+                        &xs[buf][(ms * 16 + li) * kLdsRowBf16 + 64 * lk]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const u32x4 b = bp[c];
+                        acc_a[ms] = mfma_bf16(wa_cur[c], b, acc_a[ms]);
+                        acc_b[ms] = mfma_bf16(wb_cur[c], b, acc_b[ms]);
+                    }
+                }
+            }
+            if (more) {
+                u32x4* d = reinterpret_cast<u32x4*>(&xs[buf ^ 1][tr * kLdsRowBf16 + 64 * tq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[i] = xr[i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    wa_cur[i] = wa_nxt[i];
+                    wb_cur[i] = wb_nxt[i];
+                }
+            }
+            __syncthreads();
+        }
+
+        // epilogue: lane holds D[n = base + 4*lk + r][m = ms*16 + li]
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+            const int m = ms * 16 + li;
+            if (ms < nms && m < tile.rows) {
+                uint16_t* orow = out + (size_t)(tile.row0 + m) * ldo;
+                if (kSwiGLU) {
+                    const int col = nb * 64 + 16 * wave + 4 * lk;
+                    float a0 = silu_mul(acc_a[ms][0], acc_b[ms][0]);
+                    float a1 = silu_mul(acc_a[ms][1], acc_b[ms][1]);
+                    float a2 = silu_mul(acc_a[ms][2], acc_b[ms][2]);
+                    float a3 = silu_mul(acc_a[ms][3], acc_b[ms][3]);
+                    *reinterpret_cast<uint2*>(orow + col) =
+                        make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
+                } else {
+                    const int col = nb * 128 + 32 * wave + 4 * lk;
+                    *reinterpret_cast<uint2*>(orow + col) =
+                        make_uint2(pack_bf16x2(acc_a[ms][0], acc_a[ms][1]),
+                                   pack_bf16x2(acc_a[ms][2], acc_a[ms][3]));
+                    *reinterpret_cast<uint2*>(orow + col + 16) =
+                        make_uint2(pack_bf16x2(acc_b[ms][0], acc_b[ms][1]),
+                                   pack_bf16x2(acc_b[ms][2], acc_b[ms][3]));
+                }
+            }
+        }
+    }
+}
+
+// ============================================================================ fp8
+// SwiGLU (GEMM-1): an item covers 128 intermediate columns = one 1x128 output
+//   quantisation block; wave w owns gate rows n0+32w+{0,16}+li and the up rows
+//   I + the same (n0 = nb*128). Output: A codes [rows][I] + scales [rows][I/128].
+// Down (GEMM-2): an item covers 256 output columns; wave w owns rows
+//   n0+64w+16s+li, s = 0..3 (n0 = nb*256). Output: y [rows][H] bf16.
+constexpr int kLdsRowFp8 = kBK + 16;  // bytes per staged activation row
+
+template <bool kSwiGLU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gemm_fp8_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
+    const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
+    int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
+    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
+    __shared__ TileMap tm;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kBM * kLdsRowFp8];
+    __shared__ float xsc[2][kBM];
+    __shared__ float red[4][kBM];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int nk = K / kBK;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows) * NB;
+    const int kbn = K / kBK;  // scale blocks along K
+
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB);
+        const int nb = item % NB;
+        const bool routed = tile.group < n_routed;
+        const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
+        const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * kbn : Wsh_sc;
+        int row[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (kSwiGLU) row[s] = nb * 128 + 32 * wave + 16 * (s & 1) + li + (s >> 1) * (Nw / 2);
+            else row[s] = nb * 256 + 64 * wave + 16 * s + li;
+        }
+        const uint8_t* wp[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) wp[s] = Wg + (size_t)row[s] * K + 32 * lk;
+        // scale row block of each subtile (all 16 rows share one 128-row block)
+        int sblk[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sblk[s] = (row[s] - li) / kBK;
+        const int nms = (tile.rows + 15) >> 4;
+
+        // staging: thread -> (row tr, 32-byte quarter tq)
+        const int tr = threadIdx.x >> 2, tq = threadIdx.x & 3;
+        const bool xin = tr < tile.rows;
+        const uint8_t* xsrc = X + (size_t)(tile.row0 + (xin ? tr : 0)) * K + 32 * tq;
+        const float* ssrc = Xs + (size_t)(tile.row0 + (xin ? tr : 0)) * kbn;
+
+        f32x4 acc[4][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        i32x8 w_cur[4], w_nxt[4];
+        u32x4 xr[2];
+        float xsr = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w_cur[s] = *reinterpret_cast<const i32x8*>(wp[s]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc)[i] : u32x4{0, 0, 0, 0};
+        if (tq == 0) xsr = xin ? ssrc[0] : 0.f;
+        {
+            u32x4* d = reinterpret_cast<u32x4*>(&xs[0][tr * kLdsRowFp8 + 32 * tq]);
+            d[0] = xr[0];
+            d[1] = xr[1];
+            if (tq == 0) xsc[0][tr] = xsr;
+        }
+        __syncthreads();
+
+        for (int kc = 0; kc < nk; ++kc) {
+            const int buf = kc & 1;
+            const bool more = kc + 1 < nk;
+            if (more) {
+                const int ko = (kc + 1) * kBK;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) w_nxt[s] = *reinterpret_cast<const i32x8*>(wp[s] + ko);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc + ko)[i] : u32x4{0, 0, 0, 0};
+                if (tq == 0) xsr = xin ? ssrc[kc + 1] : 0.f;
+            }
+            float sw[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) sw[s] = Sg[(size_t)sblk[s] * kbn + kc];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                if (ms < nms) {
+                    const i32x8 b = *reinterpret_cast<const i32x8*>(
+                        &xs[buf][(ms * 16 + li) * kLdsRowFp8 + 32 * lk]);
+                    const float sx = xsc[buf][ms * 16 + li];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const f32x4 p = mfma_fp8(w_cur[s], b);
+                        const float f = sw[s] * sx;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[s][ms][r] = __builtin_fmaf(p[r], f, acc[s][ms][r]);
+                    }
+                }
+            }
+            if (more) {
+                u32x4* d = reinterpret_cast<u32x4*>(&xs[buf ^ 1][tr * kLdsRowFp8 + 32 * tq]);
+                d[0] = xr[0];
+                d[1] = xr[1];
+                if (tq == 0) xsc[buf ^ 1][tr] = xsr;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) w_cur[s] = w_nxt[s];
+            }
+            __syncthreads();
+        }
+
+        // epilogue: lane holds D[n = row base + 4*lk + r][m = ms*16 + li]
+        //   NOTE the accumulator rows are n = (row[s] - li) + 4*lk + r.
+        if (kSwiGLU) {
+            float a[2][4][4];  // [gate subtile][ms][r]
+            float amax[4];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                float mx = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        a[h][ms][r] = silu_mul(acc[h][ms][r], acc[2 + h][ms][r]);
+                        mx = fmaxf(mx, fabsf(a[h][ms][r]));
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                amax[ms] = mx;
+            }
+            if (lk == 0) {
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms) red[wave][ms * 16 + li] = amax[ms];
+            }
+            __syncthreads();
+            uint8_t* codes = reinterpret_cast<uint8_t*>(out);
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                const int m = ms * 16 + li;
+                if (ms < nms && m < tile.rows) {
+                    const float mx = fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m]));
+                    const float sc = block_scale(mx);
+                    uint8_t* orow = codes + (size_t)(tile.row0 + m) * ldo;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int col = nb * 128 + 32 * wave + 16 * h + 4 * lk;
+                        *reinterpret_cast<uint32_t*>(orow + col) =
+                            pack_e4m3x4(clamp_e4m3(a[h][ms][0] / sc), clamp_e4m3(a[h][ms][1] / sc),
+                                        clamp_e4m3(a[h][ms][2] / sc), clamp_e4m3(a[h][ms][3] / sc));
+                    }
+                    if (wave == 0 && lk == 0) out_scale[(size_t)(tile.row0 + m) * (ldo / kBK) + nb] = sc;
+                }
+            }
+            __syncthreads();  // red[] is reused by the next item
+        } else {
+            uint16_t* y = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                const int m = ms * 16 + li;
+                if (ms < nms && m < tile.rows) {
+                    uint16_t* orow = y + (size_t)(tile.row0 + m) * ldo;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int col = nb * 256 + 64 * wave + 16 * s + 4 * lk;
+                        *reinterpret_cast<uint2*>(orow + col) =
+                            make_uint2(pack_bf16x2(acc[s][ms][0], acc[s][ms][1]),
+                                       pack_bf16x2(acc[s][ms][2], acc[s][ms][3]));
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ============================================================================ fp32
+// Plain VALU kernels for fp32 layers (small shapes): one thread per output.
+__device__ __forceinline__ int group_of(const int32_t* offsets, int n_groups, int r) {
+    int g = 0;
+    while (g + 1 < n_groups && offsets[g + 1] <= r) ++g;
+    return g;
+}
+
+__global__ void ffn_gemm1_f32_kernel(const float* __restrict__ X, const float* __restrict__ W,
+                                     const float* __restrict__ Ws, int n_routed,
+                                     const int32_t* __restrict__ offsets, int n_groups, int max_rows,
+                                     int H, int I, float* __restrict__ A) {
+    const long n = (long)min(offsets[n_groups], max_rows) * I;
+    for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (long)gridDim.x * blockDim.x) {
+        const int r = (int)(idx / I), i = (int)(idx % I);
+        const int g = group_of(offsets, n_groups, r);
+        const float* Wg = g < n_routed ? W + (size_t)g * 2 * I * H : Ws;
+        const float* x = X + (size_t)r * H;
+        float gs = 0.f, us = 0.f;
+        for (int h = 0; h < H; ++h) {
+            gs = __builtin_fmaf(x[h], Wg[(size_t)i * H + h], gs);
+            us = __builtin_fmaf(x[h], Wg[(size_t)(I + i) * H + h], us);
+        }
+        A[idx] = silu_mul(gs, us);
+    }
+}
+
+__global__ void ffn_gemm2_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
+                                     const float* __restrict__ Ws, int n_routed,
+                                     const int32_t* __restrict__ offsets, int n_groups, int max_rows,
+                                     int H, int I, float* __restrict__ Y) {
+    const long n = (long)min(offsets[n_groups], max_rows) * H;
+    for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (long)gridDim.x * blockDim.x) {
+        const int r = (int)(idx / H), h = (int)(idx % H);
+        const int g = group_of(offsets, n_groups, r);
+        const float* Wg = g < n_routed ? W + (size_t)g * H * I : Ws;
+        const float* a = A + (size_t)r * I;
+        float y = 0.f;
+        for (int i = 0; i < I; ++i) y = __builtin_fmaf(a[i], Wg[(size_t)h * I + i], y);
+        Y[idx] = y;
+    }
+}
+
+struct FfnWs {
+    void* a;        // intermediate activations A [max_rows][I]
+    float* a_scale; // fp8 only: [max_rows][I/128]
+    size_t bytes;
+};
+
+FfnWs carve(const moe_expert_weights* w, int max_rows, void* base) {
+    size_t off = 0;
+    FfnWs r{};
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes, 256);
+        return base ? (void*)((uint8_t*)base + o) : nullptr;
+    };
+    size_t eb = w->dt == MOE_F32 ? 4 : w->dt == MOE_BF16 ? 2 : 1;
+    r.a = take((size_t)max_rows * w->I * eb);
+    r.a_scale = w->dt == MOE_FP8_E4M3 ? (float*)take((size_t)max_rows * (w->I / kBK) * 4) : nullptr;
+    r.bytes = off > 0 ? off : 256;
+    return r;
+}
+
+int persistent_grid(long bound, int per_cu) {
+    const long cap = (long)device_info().cu_count * per_cu;
+    long g = bound < cap ? bound : cap;
+    return (int)(g > 0 ? g : 1);
+}
+
+}  // namespace
+
+size_t ffn_workspace_bytes(const moe_expert_weights* w, int max_rows) {
+    return carve(w, max_rows, nullptr).bytes;
+}
+
+moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
+                              const float* x_perm_scale, const int32_t* offsets, int n_groups,
+                              int max_rows, void* ws, hipStream_t st) {
+    FfnWs s = carve(w, max_rows, ws);
+    const int H = w->H, I = w->I, E = w->E_local;
+    const long tiles_bound = (long)(max_rows + kBM - 1) / kBM + n_groups;
+    if (w->dt == MOE_F32) {
+        const int blocks = persistent_grid(((long)max_rows * I + 255) / 256, 8);
+        hipLaunchKernelGGL(ffn_gemm1_f32_kernel, dim3(blocks), dim3(256), 0, st, (const float*)x_perm,
+                           (const float*)w->w13, (const float*)w->ws13, E, offsets, n_groups, max_rows,
+                           H, I, (float*)s.a);
+        return check_launch("ffn_gemm1_f32_kernel");
+    }
+    if (w->dt == MOE_BF16) {
+        const int NB = I / 64;
+        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<true>, dim3(persistent_grid(tiles_bound * NB, 3)),
+                           dim3(kThreads), 0, st, (const uint16_t*)x_perm, (const uint16_t*)w->w13,
+                           (const uint16_t*)w->ws13, E, offsets, n_groups, max_rows, H, 2 * I, NB,
+                           (uint16_t*)s.a, I);
+        return check_launch("ffn_gemm_bf16_kernel<gate_up>");
+    }
+    const int NB = I / 128;
+    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<true>, dim3(persistent_grid(tiles_bound * NB, 2)),
+                       dim3(kThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
+                       (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E,
+                       offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale, I);
+    return check_launch("ffn_gemm_fp8_kernel<gate_up>");
+}
+
+moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, int n_groups,
+                           int max_rows, void* y_perm, void* ws, hipStream_t st) {
+    FfnWs s = carve(w, max_rows, ws);
+    const int H = w->H, I = w->I, E = w->E_local;
+    const long tiles_bound = (long)(max_rows + kBM - 1) / kBM + n_groups;
+    if (w->dt == MOE_F32) {
+        const int blocks = persistent_grid(((long)max_rows * H + 255) / 256, 8);
+        hipLaunchKernelGGL(ffn_gemm2_f32_kernel, dim3(blocks), dim3(256), 0, st, (const float*)s.a,
+                           (const float*)w->w2, (const float*)w->ws2, E, offsets, n_groups, max_rows,
+                           H, I, (float*)y_perm);
+        return check_launch("ffn_gemm2_f32_kernel");
+    }
+    if (w->dt == MOE_BF16) {
+        const int NB = H / 128;
+        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<false>, dim3(persistent_grid(tiles_bound * NB, 3)),
+                           dim3(kThreads), 0, st, (const uint16_t*)s.a, (const uint16_t*)w->w2,
+                           (const uint16_t*)w->ws2, E, offsets, n_groups, max_rows, I, H, NB,
+                           (uint16_t*)y_perm, H);
+        return check_launch("ffn_gemm_bf16_kernel<down>");
+    }
+    const int NB = H / 256;
+    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<false>, dim3(persistent_grid(tiles_bound * NB, 2)),
+                       dim3(kThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
+                       w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
+                       max_rows, I, H, NB, y_perm, nullptr, H);
+    return check_launch("ffn_gemm_fp8_kernel<down>");
+}
+
+}  // namespace moe

@@ -1,0 +1,253 @@
+// Token -> expert grouping ([Moreh-EP] Library optimization: the fused MoE
+// kernel consumes tokens grouped by expert; Inter-GPU load balancing: the
+// per-expert activation counts). Deterministic, with atomics used only to
+// count or to set bits, never to hand out positions.
+//
+//   hist     one workgroup per chunk of 1024 slots: LDS histogram of the
+//            local experts -> chunk_counts[chunk][e]
+//   scan     one workgroup: per expert an exclusive scan over chunks, then an
+//            exclusive scan over experts (+ the shared group) -> counts,
+//            offsets, and chunk_base[chunk][e] = first row of that chunk's
+//            slots of expert e
+//   scatter  one workgroup per chunk: an LDS bitmap of the chunk's slots per
+//            expert; the rank of a slot among its expert's slots is a popcount
+//            of the bits below it, so rows come out in (expert, slot) order
+//   fill     rows past the routed ones: shared-expert rows, then -1
+//   gather   x_perm[row] = x[token(row)] (bit copy or 1x128 e4m3 quantisation)
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;   // slots per chunk
+constexpr int kMaxLocal = 256; // local experts handled per launch
+
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, long S,
+                                                        int base, int E_local,
+                                                        int32_t* __restrict__ chunk_counts) {
+    __shared__ int cnt[kMaxLocal];
+    for (int e = threadIdx.x; e < E_local; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const long s0 = (long)blockIdx.x * kChunk;
+    for (int i = threadIdx.x; i < kChunk; i += 256) {
+        long s = s0 + i;
+        if (s < S) {
+            int e = ids[s] - base;
+            if (e >= 0 && e < E_local) atomicAdd(&cnt[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E_local; e += 256)
+        chunk_counts[(size_t)blockIdx.x * E_local + e] = cnt[e];
+}
+
+// single workgroup of 256 threads
+__global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ chunk_counts,
+                                                        int n_chunks, int E_local, int n_shared,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets) {
+    __shared__ int tot[kMaxLocal + 1];
+    __shared__ int excl[kMaxLocal + 2];
+    const int e = threadIdx.x;
+    if (e < E_local) {
+        int run = 0;
+        for (int c = 0; c < n_chunks; ++c) {
+            int v = chunk_counts[(size_t)c * E_local + e];
+            chunk_counts[(size_t)c * E_local + e] = run;
+            run += v;
+        }
+        tot[e] = run;
+    }
+    if (e == 0) tot[E_local] = n_shared;
+    __syncthreads();
+    if (e == 0) {  // E_local + 1 <= 257 values: a serial scan is cheapest here
+        int run = 0;
+        for (int g = 0; g <= E_local; ++g) {
+            excl[g] = run;
+            run += tot[g];
+        }
+        excl[E_local + 1] = run;
+    }
+    __syncthreads();
+    if (e < E_local) {
+        counts[e] = tot[e];
+        offsets[e] = excl[e];
+        const int o = excl[e];
+        for (int c = 0; c < n_chunks; ++c) chunk_counts[(size_t)c * E_local + e] += o;
+    }
+    if (e == 0) {
+        counts[E_local] = n_shared;
+        offsets[E_local] = excl[E_local];
+        offsets[E_local + 1] = excl[E_local + 1];
+    }
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, long S,
+                                                           int base, int E_local,
+                                                           const int32_t* __restrict__ chunk_base,
+                                                           int32_t* __restrict__ row_to_slot,
+                                                           int32_t* __restrict__ slot_to_row) {
+    constexpr int kWords = kChunk / 32;
+    __shared__ uint32_t bits[kMaxLocal][kWords];
+    __shared__ int pre[kMaxLocal][kWords];
+    for (int i = threadIdx.x; i < E_local * kWords; i += 256) bits[i / kWords][i % kWords] = 0;
+    __syncthreads();
+    const long s0 = (long)blockIdx.x * kChunk;
+    int my_e[kChunk / 256];
+#pragma unroll
+    for (int q = 0; q < kChunk / 256; ++q) {
+        const int p = threadIdx.x + 256 * q;
+        const long s = s0 + p;
+        int e = -1;
+        if (s < S) {
+            e = ids[s] - base;
+            if (e < 0 || e >= E_local) e = -1;
+        }
+        my_e[q] = e;
+        if (e >= 0) atomicOr(&bits[e][p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E_local; e += 256) {
+        int run = 0;
+        for (int w = 0; w < kWords; ++w) {
+            pre[e][w] = run;
+            run += __popc(bits[e][w]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kChunk / 256; ++q) {
+        const int p = threadIdx.x + 256 * q;
+        const long s = s0 + p;
+        if (s >= S) continue;
+        const int e = my_e[q];
+        if (e < 0) {
+            slot_to_row[s] = -1;
+            continue;
+        }
+        const int w = p >> 5;
+        const int rank = pre[e][w] + __popc(bits[e][w] & ((1u << (p & 31)) - 1u));
+        const int row = chunk_base[(size_t)blockIdx.x * E_local + e] + rank;
+        row_to_slot[row] = (int32_t)s;
+        slot_to_row[s] = row;
+    }
+}
+
+__global__ void perm_fill_kernel(const int32_t* __restrict__ offsets, int E_local, long S,
+                                 long cap, int32_t* __restrict__ row_to_slot) {
+    const long R = offsets[E_local];
+    const long used = offsets[E_local + 1];
+    for (long r = R + (long)blockIdx.x * blockDim.x + threadIdx.x; r < cap;
+         r += (long)gridDim.x * blockDim.x)
+        row_to_slot[r] = r < used ? (int32_t)(S + (r - R)) : -1;
+}
+
+__device__ __forceinline__ long token_of(int32_t slot, long S, int k) {
+    return slot < S ? slot / k : slot - S;
+}
+
+// bit copy of rows; elem_bytes in {2, 4}
+__global__ __launch_bounds__(256) void perm_gather_copy_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ row_to_slot,
+    const int32_t* __restrict__ offsets, int E_local, long S, int k, long row_bytes,
+    uint8_t* __restrict__ x_perm) {
+    const long used = offsets[E_local + 1];
+    for (long r = blockIdx.x; r < used; r += gridDim.x) {
+        const long t = token_of(row_to_slot[r], S, k);
+        const uint8_t* src = x + t * row_bytes;
+        uint8_t* dst = x_perm + r * row_bytes;
+        if ((row_bytes & 15) == 0) {
+            for (long i = threadIdx.x; i < row_bytes / 16; i += blockDim.x)
+                reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+        } else {
+            for (long i = threadIdx.x; i < row_bytes / 2; i += blockDim.x)
+                reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(src)[i];
+        }
+    }
+}
+
+// bf16 rows -> e4m3 codes + one fp32 scale per 128 elements; H % 128 == 0.
+// 16 lanes own one 128-element block, 8 elements each.
+__global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ row_to_slot,
+    const int32_t* __restrict__ offsets, int E_local, long S, int k, int H,
+    uint8_t* __restrict__ x_perm, float* __restrict__ x_scale) {
+    const long used = offsets[E_local + 1];
+    const int nb = H / 128;
+    const int sub = threadIdx.x & 15;
+    for (long r = blockIdx.x; r < used; r += gridDim.x) {
+        const long t = token_of(row_to_slot[r], S, k);
+        const uint16_t* src = x + t * H;
+        for (int b = threadIdx.x >> 4; b < nb; b += 16) {
+            const int h0 = b * 128 + sub * 8;
+            u32x4 q = *reinterpret_cast<const u32x4*>(src + h0);
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16_lo(q[i]);
+                v[2 * i + 1] = bf16_hi(q[i]);
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+            for (int s = 8; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
+            const float sc = block_scale(a);
+            float qv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[i] = clamp_e4m3(v[i] / sc);
+            uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
+            uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
+            *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
+            if (sub == 0) x_scale[r * nb + b] = sc;
+        }
+    }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int T, int k, int E_local) {
+    long S = (long)T * k;
+    long n_chunks = (S + kChunk - 1) / kChunk;
+    return align_up((size_t)(n_chunks > 0 ? n_chunks : 1) * E_local * sizeof(int32_t), 256);
+}
+
+moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_local, int include_shared,
+                          const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt, int32_t* counts,
+                          int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                          void* x_perm, float* x_perm_scale, void* ws, hipStream_t st) {
+    const long S = (long)T * k;
+    const long cap = S + T;
+    const int n_chunks = (int)((S + kChunk - 1) / kChunk);
+    int32_t* chunk_counts = (int32_t*)ws;
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(n_chunks), dim3(256), 0, st, ids, S, base, E_local,
+                       chunk_counts);
+    moe_status s = check_launch("perm_hist_kernel");
+    if (s) return s;
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, st, chunk_counts, n_chunks, E_local,
+                       include_shared ? T : 0, counts, offsets);
+    if ((s = check_launch("perm_scan_kernel"))) return s;
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(n_chunks), dim3(256), 0, st, ids, S, base, E_local,
+                       chunk_counts, row_to_slot, slot_to_row);
+    if ((s = check_launch("perm_scatter_kernel"))) return s;
+    const int fill_blocks = (int)std::min<long>((cap + 255) / 256, 1024);
+    hipLaunchKernelGGL(perm_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, offsets, E_local, S, cap,
+                       row_to_slot);
+    if ((s = check_launch("perm_fill_kernel"))) return s;
+    if (!x_perm) return MOE_OK;
+    const int cu = device_info().cu_count;
+    const int gather_blocks = (int)std::min<long>(cap, (long)cu * 8);
+    if (perm_dt == MOE_FP8_E4M3) {
+        hipLaunchKernelGGL(perm_gather_fp8_kernel, dim3(gather_blocks), dim3(256), 0, st,
+                           (const uint16_t*)x, row_to_slot, offsets, E_local, S, k, H,
+                           (uint8_t*)x_perm, x_perm_scale);
+        return check_launch("perm_gather_fp8_kernel");
+    }
+    const long eb = x_dt == MOE_F32 ? 4 : 2;
+    hipLaunchKernelGGL(perm_gather_copy_kernel, dim3(gather_blocks), dim3(256), 0, st,
+                       (const uint8_t*)x, row_to_slot, offsets, E_local, S, k, eb * H,
+                       (uint8_t*)x_perm);
+    return check_launch("perm_gather_copy_kernel");
+}
+
+}  // namespace moe

@@ -1,0 +1,133 @@
+"""One MoE layer on one GPU: buffers plus the four C-ABI calls in order.
+
+route -> permute -> expert FFN -> combine ([Moreh-EP] Overview and
+Parallelization: gating picks k experts per token, the expert FFNs run on the
+tokens routed to them, an always-on shared expert runs on every token, and
+the results are combined with the routing weights). This module only
+allocates device buffers (torch) and passes pointers to libmoe.so; all
+arithmetic happens in the library's kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class LayerBuffers:
+    T: int
+    logits: Optional[torch.Tensor]
+    topk_ids: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    row_to_slot: torch.Tensor
+    slot_to_row: torch.Tensor
+    x_perm: torch.Tensor
+    x_perm_scale: Optional[torch.Tensor]
+    y_perm: torch.Tensor
+    out: torch.Tensor
+    ws_perm: torch.Tensor
+    ws_ffn: torch.Tensor
+
+
+class MoELayer:
+    """Weights of one GPU's expert share (+ optional shared expert and router).
+
+    fmt: "f32", "bf16" or "fp8". Expert weights are device tensors
+    w13 [E_local, 2I, H], w2 [E_local, H, I] (uint8 e4m3 codes for fp8, with
+    w13_scale [E_local, 2I/128, H/128], w2_scale [E_local, H/128, I/128]).
+    router: dict(w=[E, H], bias=[E] or None, scoring, renormalize) or None
+    when the routing is handed in (expert-parallel share).
+    """
+
+    def __init__(self, fmt: str, H: int, I: int, k: int, w13, w2, w13_scale=None, w2_scale=None,
+                 shared: Optional[dict] = None, router: Optional[dict] = None, expert_base: int = 0):
+        self.fmt = fmt
+        self.H, self.I, self.k = H, I, k
+        self.E_local = w13.shape[0]
+        self.expert_base = expert_base
+        self.dt = {"f32": L.F32, "bf16": L.BF16, "fp8": L.FP8_E4M3}[fmt]
+        self.act_dt = L.F32 if fmt == "f32" else L.BF16
+        self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
+        self.shared = shared
+        self.router = router
+        sh = shared or {}
+        self.weights = L.make_weights(self.dt, self.E_local, H, I, w13, w2, w13_scale, w2_scale,
+                                      sh.get("w13"), sh.get("w2"), sh.get("w13_scale"),
+                                      sh.get("w2_scale"))
+        self.n_groups = self.E_local + (1 if shared is not None else 0)
+        self._bufs = {}
+
+    # ------------------------------------------------------------------ buffers
+    def buffers(self, T: int, device=None) -> LayerBuffers:
+        if T in self._bufs:
+            return self._bufs[T]
+        device = device or self.w13.device
+        k, H = self.k, self.H
+        cap = T * k + T
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        act = torch.float32 if self.fmt == "f32" else torch.bfloat16
+        E = self.router["w"].shape[0] if self.router is not None else 0
+        xdt = torch.uint8 if self.fmt == "fp8" else act
+        ws_p = L.moe_permute_workspace_size(T, k, self.E_local)
+        ws_f = L.moe_expert_ffn_workspace_size(self.weights, cap)
+        b = LayerBuffers(
+            T=T,
+            logits=torch.empty((T, E), **f32) if E else None,
+            topk_ids=torch.empty((T, k), **i32),
+            topk_w=torch.empty((T, k), **f32),
+            counts=torch.empty(self.E_local + 1, **i32),
+            offsets=torch.empty(self.E_local + 2, **i32),
+            row_to_slot=torch.empty(cap, **i32),
+            slot_to_row=torch.empty(T * k, **i32),
+            x_perm=torch.empty((cap, H), dtype=xdt, device=device),
+            x_perm_scale=torch.empty((cap, H // 128), **f32) if self.fmt == "fp8" else None,
+            y_perm=torch.empty((cap, H), dtype=act, device=device),
+            out=torch.empty((T, H), dtype=act, device=device),
+            ws_perm=torch.empty(max(ws_p, 1), dtype=torch.uint8, device=device),
+            ws_ffn=torch.empty(max(ws_f, 1), dtype=torch.uint8, device=device),
+        )
+        self._bufs[T] = b
+        return b
+
+    # ------------------------------------------------------------------ steps
+    def route(self, x: torch.Tensor, b: LayerBuffers, stream=None):
+        r = self.router
+        T, H = x.shape
+        E = r["w"].shape[0]
+        L.moe_route(x, r["w"], r.get("bias"), self.act_dt, T, H, E, self.k, r["scoring"],
+                    r.get("renormalize", True), b.logits, b.topk_ids, b.topk_w, stream)
+
+    def permute(self, x: torch.Tensor, b: LayerBuffers, topk_ids=None, stream=None):
+        T = x.shape[0]
+        ids = b.topk_ids if topk_ids is None else topk_ids
+        L.moe_permute(ids, T, self.k, self.expert_base, self.E_local, self.shared is not None, x,
+                      self.act_dt, self.H, self.dt if self.fmt == "fp8" else self.act_dt, b.counts,
+                      b.offsets, b.row_to_slot, b.slot_to_row, b.x_perm, b.x_perm_scale, b.ws_perm,
+                      b.ws_perm.numel(), stream)
+
+    def ffn(self, b: LayerBuffers, stream=None):
+        cap = b.T * self.k + b.T
+        L.moe_expert_ffn(self.weights, b.x_perm, b.x_perm_scale, b.offsets, self.n_groups, cap,
+                         b.y_perm, b.ws_ffn, b.ws_ffn.numel(), stream)
+
+    def combine(self, b: LayerBuffers, topk_w=None, stream=None):
+        w = b.topk_w if topk_w is None else topk_w
+        L.moe_combine(b.y_perm, self.act_dt, b.slot_to_row, w, b.T, self.k, self.H, b.offsets,
+                      self.E_local if self.shared is not None else -1, b.out, self.act_dt, stream)
+
+    def forward(self, x: torch.Tensor, topk_ids=None, topk_w=None, stream=None) -> LayerBuffers:
+        """The whole layer. Routing comes from the router unless given."""
+        b = self.buffers(x.shape[0], x.device)
+        if topk_ids is None:
+            self.route(x, b, stream)
+        self.permute(x, b, topk_ids, stream)
+        self.ffn(b, stream)
+        self.combine(b, topk_w, stream)
+        return b

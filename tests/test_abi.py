@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, rejects bad arguments before touching a device, sizes its workspaces,
+and its host-side balanced partition matches the oracle bit for bit."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import mixture_experts_layer_select_amd as pkg
+    if not os.path.exists(pkg._lib.LIB_PATH):
+        pkg.build()
+    return pkg
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    lib = C.CDLL(L._lib.LIB_PATH)
+    names = _declared()
+    assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+            "moe_balanced_partition"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def _expect(L, fn, status, *args):
+    with pytest.raises(L.MoEError) as ei:
+        fn(*args)
+    assert ei.value.status == status, str(ei.value)
+    return str(ei.value)
+
+
+def test_route_argument_checks(L):
+    big = dict(T=4, H=64, E=300, k=8)
+    msg = _expect(L, L.moe_route, "MOE_ERR_UNSUPPORTED", 1, 1, None, L.BF16, 4, 64, 300, 8, L.SIGMOID,
+                  1, 1, 1, 1, 0)
+    assert "E=300" in msg
+    _expect(L, L.moe_route, "MOE_ERR_INVALID_ARG", 1, 1, None, L.BF16, 4, 64, 16, 17, L.SIGMOID, 1,
+            1, 1, 1, 0)
+    _expect(L, L.moe_route, "MOE_ERR_INVALID_ARG", None, 1, None, L.BF16, 4, 64, 16, 2, L.SIGMOID, 1,
+            1, 1, 1, 0)
+    _expect(L, L.moe_route, "MOE_ERR_UNSUPPORTED", 1, 1, None, L.FP8_E4M3, 4, 64, 16, 2, L.SIGMOID,
+            1, 1, 1, 1, 0)
+    _expect(L, L.moe_route, "MOE_ERR_INVALID_ARG", 1, 1, None, L.BF16, -1, 64, 16, 2, L.SIGMOID, 1,
+            1, 1, 1, 0)
+    # T == 0 is a no-op that needs no pointers at all
+    L.moe_route(None, None, None, L.BF16, 0, 64, 16, 2, L.SIGMOID, 1, None, None, None, 0)
+
+
+def test_permute_argument_checks(L):
+    ws = L.moe_permute_workspace_size(100, 8, 32)
+    assert ws >= 4 * 32 and ws % 256 == 0
+    _expect(L, L.moe_permute, "MOE_ERR_UNSUPPORTED", 1, 100, 8, 0, 300, 0, None, L.BF16, 0, L.BF16,
+            1, 1, 1, 1, None, None, 1, ws, 0)
+    _expect(L, L.moe_permute, "MOE_ERR_WORKSPACE", 1, 100, 8, 0, 32, 0, None, L.BF16, 0, L.BF16,
+            1, 1, 1, 1, None, None, 1, ws - 1, 0)
+    _expect(L, L.moe_permute, "MOE_ERR_UNSUPPORTED", 1, 100, 8, 0, 32, 0, 1, L.BF16, 100,
+            L.FP8_E4M3, 1, 1, 1, 1, 1, 1, 1, ws, 0)   # fp8 needs H % 128
+    _expect(L, L.moe_permute, "MOE_ERR_INVALID_ARG", 1, 100, 8, 0, 32, 0, 1, L.BF16, 128,
+            L.FP8_E4M3, 1, 1, 1, 1, 1, None, 1, ws, 0)  # fp8 needs scales
+    _expect(L, L.moe_permute, "MOE_ERR_INVALID_ARG", None, 100, 8, 0, 32, 0, None, L.BF16, 0,
+            L.BF16, 1, 1, 1, 1, None, None, 1, ws, 0)
+    L.moe_permute(None, 0, 8, 0, 32, 1, None, L.BF16, 0, L.BF16, None, None, None, None, None, None,
+                  None, 0, 0)
+
+
+def test_ffn_argument_checks_and_workspace(L):
+    w = L.make_weights(L.BF16, 32, 7168, 2048, 1, 1)
+    ws = L.moe_expert_ffn_workspace_size(w, 4096 * 9)
+    # tiles + intermediate activations (bf16) at least
+    assert ws >= 4096 * 9 * 2048 * 2
+    _expect(L, L.moe_expert_ffn, "MOE_ERR_INVALID_ARG", w, 1, None, 1, 34, 100, 1, 1, ws, 0)
+    _expect(L, L.moe_expert_ffn, "MOE_ERR_INVALID_ARG", w, 1, None, 1, 33, 100, 1, 1, ws, 0)  # no shared
+    _expect(L, L.moe_expert_ffn, "MOE_ERR_WORKSPACE", w, 1, None, 1, 32, 4096 * 9, 1, 1, ws - 1, 0)
+    bad = L.make_weights(L.BF16, 32, 7000, 2048, 1, 1)
+    _expect(L, L.moe_expert_ffn, "MOE_ERR_UNSUPPORTED", bad, 1, None, 1, 32, 10, 1, 1, 10 ** 9, 0)
+    f8 = L.make_weights(L.FP8_E4M3, 32, 7168, 2048, 1, 1)  # no scales
+    _expect(L, L.moe_expert_ffn, "MOE_ERR_INVALID_ARG", f8, 1, 1, 1, 32, 10, 1, 1, 10 ** 9, 0)
+    assert L.moe_expert_ffn_workspace_size(bad, 10) == 0
+
+
+def test_combine_and_gather_rows_checks(L):
+    _expect(L, L.moe_combine, "MOE_ERR_UNSUPPORTED", 1, L.FP8_E4M3, 1, 1, 4, 2, 64, None, -1, 1,
+            L.BF16, 0)
+    _expect(L, L.moe_combine, "MOE_ERR_INVALID_ARG", 1, L.BF16, 1, 1, 4, 2, 64, None, 3, 1, L.BF16, 0)
+    _expect(L, L.moe_gather_rows, "MOE_ERR_UNSUPPORTED", 1, 4, 1, 1, 4, 6, 0)
+    L.moe_combine(None, L.BF16, None, None, 0, 2, 64, None, -1, None, L.BF16, 0)
+
+
+@pytest.mark.parametrize("E,G,seed", [(6, 2, 0), (256, 8, 1), (256, 8, 2), (64, 4, 3), (12, 3, 4)])
+def test_balanced_partition_matches_oracle(L, orc, E, G, seed):
+    rng = np.random.default_rng(seed)
+    counts = rng.zipf(1.3, E).clip(max=10 ** 6).astype(np.int64)
+    counts[rng.integers(0, E, E // 4)] = 0
+    c = torch.from_numpy(counts)
+    n2o = torch.empty(E, dtype=torch.int32)
+    o2n = torch.empty(E, dtype=torch.int32)
+    loads = torch.empty(G, dtype=torch.int64)
+    L.moe_balanced_partition(c, E, G, n2o, o2n, loads)
+    r_n2o, r_o2n, r_loads = orc.balanced_partition(counts, G)
+    assert np.array_equal(n2o.numpy(), r_n2o)
+    assert np.array_equal(o2n.numpy(), r_o2n)
+    assert np.array_equal(loads.numpy(), r_loads)
+
+
+def test_balanced_partition_rejects(L):
+    c = torch.zeros(10, dtype=torch.int64)
+    n2o = torch.empty(10, dtype=torch.int32)
+    o2n = torch.empty(10, dtype=torch.int32)
+    loads = torch.empty(3, dtype=torch.int64)
+    _expect(L, L.moe_balanced_partition, "MOE_ERR_INVALID_ARG", c, 10, 3, n2o, o2n, loads)
+    c[4] = -1
+    _expect(L, L.moe_balanced_partition, "MOE_ERR_INVALID_ARG", c, 10, 2, n2o, o2n,
+            torch.empty(2, dtype=torch.int64))

@@ -1,0 +1,85 @@
+"""GPU grouped expert FFN (moe_expert_ffn) against the oracle on identical
+permuted inputs: y_perm within the layer tolerance (1e-2 bf16, 3e-2 fp8,
+1e-5 fp32) as max|gpu - oracle| / max|oracle|. Group sizes cover empty
+groups, single rows, ragged 16-row and 64-row tails and several m-tiles
+(the variable M per expert of the SGLang H20 report, SwapAB GEMM); the last
+group is the shared expert (Moreh EP report, Library optimization)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from gpu_util import DEV, cpu_dict, cpu_expert, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "fp8": 3e-2, "f32": 1e-5}
+
+
+def _run(fmt, H, I, sizes, shared, seed=0):
+    import mixture_experts_layer_select_amd as L
+    say(f"ffn fmt={fmt} H={H} I={I} sizes={sizes} shared={shared}")
+    base = {"f32": mi.CONFIGS[1], "bf16": mi.CONFIGS[2], "fp8": mi.CONFIGS[4]}[fmt]
+    cfg = mi.scaled(base, H=H, I=I, cid=100 + seed)
+    E_local = len(sizes) - (1 if shared else 0)
+    st = mi.stacked_expert_weights(cfg, range(E_local), device=DEV)
+    sh = mi.shared_weights(cfg, device=DEV) if shared else None
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offsets[-1])
+    max_rows = R + 5  # a little slack, like the T*k+T bound
+    x = mi.normal((max_rows, H), 1.0, 777 + seed, DEV, cfg.act_dtype)
+    if fmt == "fp8":
+        codes, scales = oracle.quantize_1x128(x.float().cpu().numpy())
+        xp = torch.from_numpy(codes).to(DEV)
+        xs = torch.from_numpy(scales).to(DEV)
+    else:
+        xp, xs = x, None
+    dt = {"f32": L.F32, "bf16": L.BF16, "fp8": L.FP8_E4M3}[fmt]
+    shd = sh or {}
+    w = L.make_weights(dt, E_local, H, I, st["w13"], st["w2"], st["w13_scale"], st["w2_scale"],
+                       shd.get("w13"), shd.get("w2"), shd.get("w13_scale"), shd.get("w2_scale"))
+    ws_n = L.moe_expert_ffn_workspace_size(w, max_rows)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=DEV)
+    y = torch.zeros((max_rows, H), dtype=torch.float32 if fmt == "f32" else torch.bfloat16,
+                    device=DEV)
+    off_d = torch.from_numpy(offsets).to(DEV)
+    L.moe_expert_ffn(w, xp, xs, off_d, len(sizes), max_rows, y, ws, ws_n)
+    torch.cuda.synchronize()
+    groups = [cpu_expert(st, e) if sizes[e] else None for e in range(E_local)]
+    if shared:
+        groups.append(cpu_dict(sh))
+    ref = oracle.expert_ffn(groups, xp[:R].cpu() if fmt == "fp8" else x[:R].cpu(),
+                            None if xs is None else xs[:R].cpu(), offsets, H, I)
+    got = y[:R].float().cpu().numpy()
+    for g in range(len(sizes)):
+        a, b = offsets[g], offsets[g + 1]
+        if b > a:
+            e = rel_err(got[a:b], ref[a:b])
+            assert e <= TOL[fmt], f"group {g} (rows {b - a}): rel err {e:.3e}"
+    e = rel_err(got, ref)
+    say(f"  max rel err {e:.3e}")
+    return e
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_ffn_ragged_groups(fmt):
+    _run(fmt, 512, 256, [0, 1, 17, 64, 65, 130, 16, 0, 200], shared=True)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_ffn_no_shared_many_small_groups(fmt):
+    rng = np.random.default_rng(5)
+    sizes = list(rng.integers(0, 9, 40))
+    _run(fmt, 768, 384, sizes, shared=False, seed=1)
+
+
+def test_ffn_fp32_tiny():
+    _run("f32", 64, 32, [3, 0, 5, 1, 7], shared=True)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_ffn_r1_shape_one_expert_two_tiles(fmt):
+    """H=7168, I=2048: one routed expert with 80 rows (a full 64-row tile and a
+    16-row tail) plus a 3-row shared group."""
+    _run(fmt, 7168, 2048, [80, 3], shared=True, seed=2)

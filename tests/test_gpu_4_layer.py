@@ -1,0 +1,149 @@
+"""The whole layer on the GPU (route -> permute -> expert FFN -> combine
+through the C ABI) against the oracle on the five workloads: routing,
+histogram and permutation bit-exact; outputs within 1e-2 (bf16), 3e-2
+(fp8), 1e-5 (fp32) as max|gpu - oracle| / max|oracle|, on every token for the
+small cases and on sampled tokens for the full-size ones."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from gpu_util import DEV, cpu_dict, oracle_rows, out_f64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(cfg, st, sh, router=True):
+    import mixture_experts_layer_select_amd as L
+    r = None
+    if router:
+        r = dict(w=mi.router_weight(cfg, device=DEV), bias=mi.router_bias(cfg, device=DEV),
+                 scoring=L.SIGMOID if cfg.scoring == "sigmoid" else L.SOFTMAX,
+                 renormalize=cfg.renormalize)
+    return L.MoELayer(cfg.fmt, cfg.H, cfg.I, cfg.k, st["w13"], st["w2"], st["w13_scale"],
+                      st["w2_scale"], shared=sh, router=r, expert_base=cfg.expert_base)
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_layer_tiny_fp32_all_tokens():
+    cfg = mi.CONFIGS[1]
+    say("layer c1 tiny fp32")
+    st = mi.stacked_expert_weights(cfg, range(cfg.E), device=DEV)
+    layer = _layer(cfg, st, None)
+    x = mi.tokens(cfg, device=DEV)
+    b = layer.forward(x)
+    torch.cuda.synchronize()
+    experts = [dict(w13=st["w13"][e].cpu(), w2=st["w2"][e].cpu()) for e in range(cfg.E)]
+    ref = oracle.moe_layer(x.cpu(), cfg.k, experts, None, wr=layer.router["w"].cpu(),
+                           scoring=oracle.SOFTMAX)
+    assert np.array_equal(b.topk_ids.cpu().numpy(), ref["topk_ids"])
+    assert np.array_equal(b.counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(b.row_to_slot.cpu().numpy(), ref["row_to_slot"])
+    e = rel_err(out_f64(b.out), ref["out64"])
+    say(f"  rel err {e:.3e}")
+    assert e <= 1e-5
+
+
+def _full_check(cfg, layer, b, x, st, sh, n_sample, seed=0):
+    """Routing and maps on every token, outputs on sampled tokens."""
+    T = x.shape[0]
+    lg, ids, w = oracle.route(x.cpu(), layer.router["w"].cpu(),
+                              None if layer.router["bias"] is None else layer.router["bias"].cpu(),
+                              cfg.k, oracle.SIGMOID, True)
+    assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), lg.view(np.uint32))
+    assert np.array_equal(b.topk_ids.cpu().numpy(), ids)
+    assert np.abs(b.topk_w.cpu().numpy() - w).max() <= 1e-6
+    p = oracle.permute(ids, cfg.expert_base, layer.E_local, sh is not None)
+    assert np.array_equal(b.counts.cpu().numpy(), p["counts"])
+    assert np.array_equal(b.offsets.cpu().numpy(), p["offsets"])
+    assert np.array_equal(b.slot_to_row.cpu().numpy(), p["slot_to_row"])
+    assert np.array_equal(b.row_to_slot.cpu().numpy(), p["row_to_slot"])
+    rows = np.sort(np.random.default_rng(seed).choice(T, n_sample, replace=False))
+    ref = oracle_rows(x[torch.from_numpy(rows).to(DEV)].cpu(), ids[rows], w[rows], st, sh, cfg.k,
+                      layer.E_local, cfg.expert_base, cfg.fmt)
+    e = rel_err(out_f64(b.out[torch.from_numpy(rows).to(DEV)]), ref)
+    say(f"  hit experts {int((p['counts'][:layer.E_local] > 0).sum())}, sampled rel err {e:.3e}")
+    return e
+
+
+def test_layer_r1_decode_bf16_full_size():
+    cfg = mi.CONFIGS[2]
+    say("layer c2 r1 decode bf16: drawing 256 experts + shared")
+    st = mi.stacked_expert_weights(cfg, range(cfg.E), device=DEV)
+    sh = mi.shared_weights(cfg, device=DEV)
+    layer = _layer(cfg, st, sh)
+    x = mi.tokens(cfg, device=DEV)
+    b = layer.forward(x)
+    torch.cuda.synchronize()
+    out1 = b.out.clone()
+    e = _full_check(cfg, layer, b, x, st, sh, n_sample=8)
+    assert e <= 1e-2
+    b = layer.forward(x)  # a second run is bit-identical
+    torch.cuda.synchronize()
+    assert torch.equal(out1, b.out)
+    del layer, st, sh, b
+    _free()
+
+
+def test_layer_ep_share_fp8_full_size():
+    cfg = mi.CONFIGS[3]
+    say("layer c3 EP share fp8")
+    ids, w, recv = mi.ep_share_routing(cfg, device=DEV)
+    x = mi.ep_share_tokens(cfg, len(recv), device=DEV)
+    st = mi.stacked_expert_weights(cfg, range(cfg.E_local), device=DEV)
+    layer = _layer(cfg, st, None, router=False)
+    b = layer.forward(x, topk_ids=ids, topk_w=w)
+    torch.cuda.synchronize()
+    idn = ids.cpu().numpy()
+    p = oracle.permute(idn, 0, 32, False)
+    assert np.array_equal(b.counts.cpu().numpy(), p["counts"])
+    assert np.array_equal(b.slot_to_row.cpu().numpy(), p["slot_to_row"])
+    assert np.array_equal(b.row_to_slot.cpu().numpy(), p["row_to_slot"])
+    rows = np.sort(np.random.default_rng(3).choice(len(recv), 8, replace=False))
+    ref = oracle_rows(x[torch.from_numpy(rows).to(DEV)].cpu(), idn[rows], w.cpu().numpy()[rows], st,
+                      None, cfg.k, 32, 0, "fp8")
+    e = rel_err(out_f64(b.out[torch.from_numpy(rows).to(DEV)]), ref)
+    say(f"  T_recv {len(recv)} local rows {p['offsets'][32]} sampled rel err {e:.3e}")
+    assert e <= 3e-2
+    del layer, st, b
+    _free()
+
+
+def test_layer_large_batch_fp8_full_size():
+    cfg = mi.CONFIGS[4]
+    say("layer c4 large batch fp8: drawing 256 experts + shared")
+    st = mi.stacked_expert_weights(cfg, range(cfg.E), device=DEV)
+    sh = mi.shared_weights(cfg, device=DEV)
+    layer = _layer(cfg, st, sh)
+    x = mi.tokens(cfg, device=DEV)
+    b = layer.forward(x)
+    torch.cuda.synchronize()
+    e = _full_check(cfg, layer, b, x, st, sh, n_sample=6, seed=1)
+    c = b.counts.cpu().numpy()[: cfg.E]
+    say(f"  expert rows min {c.min()} median {int(np.median(c))} max {c.max()}")
+    assert e <= 3e-2
+    del layer, st, sh, b
+    _free()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_layer_small_every_token(fmt):
+    """A reduced R1-style layer checked on every token (both precisions)."""
+    base = mi.CONFIGS[2] if fmt == "bf16" else mi.CONFIGS[4]
+    cfg = mi.scaled(base, T=70, H=512, E=24, I=256, k=6)
+    say(f"layer small {fmt}")
+    st = mi.stacked_expert_weights(cfg, range(cfg.E), device=DEV)
+    sh = mi.shared_weights(cfg, device=DEV)
+    layer = _layer(cfg, st, sh)
+    x = mi.tokens(cfg, device=DEV)
+    b = layer.forward(x)
+    torch.cuda.synchronize()
+    e = _full_check(cfg, layer, b, x, st, sh, n_sample=cfg.T)
+    assert e <= (1e-2 if fmt == "bf16" else 3e-2)
