@@ -26,6 +26,8 @@
 //       block; the fp32 block scales multiply each partial product.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -127,10 +129,38 @@ __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b) {
 //   out = A [rows][I] bf16 = silu(gate) * up
 // Down (GEMM-2): W = w2 [G][H][K=I]; an item covers 128 output columns:
 //   wave w owns rows n0+32w.. and n0+32w+16.. (n0 = nb*128); out = y [rows][H]
+//
+// Items are (m-tile of <= 64 rows, n-block); the 64 x 128 activation tile of
+// a K step is shared through LDS by the 4 waves, and each wave reuses its
+// weight registers for all m-subtiles, so an expert's weights cross HBM once
+// per 64 rows. Pipeline per K step (128): a wave first issues the activation
+// loads of step j+1 (4 x 16 B per lane, only for tile rows it owns), then the
+// weight loads of step j+2 into a 3-deep register ring (8 x 16 B per lane),
+// computes step j, waits for the activations only (the 8 weight loads may
+// stay in flight: vmcnt 8), stores them to the other LDS buffer and meets the
+// other waves at a bare barrier (no memory fence, which would drain the ring).
+// Weight load c of a step reads 64 contiguous bytes of each of the wave's 16
+// rows: MFMA c takes k = 32c + 8lk + [0, 8) from lane (li, lk), for the
+// weights and the activations alike.
 constexpr int kLdsRowBf16 = kBK * 2 + 16;  // bytes per staged activation row (16 B pad)
 
+// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt, lgkmcnt at max)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// this wave's LDS accesses done (lgkmcnt 0), other counters free
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// a workgroup barrier without the release/acquire fences of __syncthreads()
+__device__ __forceinline__ void barrier_only() {
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+}
+
 template <bool kSwiGLU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void ffn_gemm_bf16_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ws,
     int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
     int NB, uint16_t* __restrict__ out, int ldo) {
@@ -139,16 +169,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int li = lane & 15;   // row of the 16x? operand piece
-    const int lk = lane >> 4;   // which 32-wide K quarter of the step
+    const int li = lane & 15;
+    const int lk = lane >> 4;
     const int nk = K / kBK;
     const int n_items = build_tile_map(tm, offsets, n_groups, max_rows) * NB;
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin
+    // (blockIdx % 8); each XCD walks a contiguous slice of the items, so the
+    // n-blocks of one m-tile (same activations) share that XCD's L2. If the
+    // dealing differs only locality suffers. The grid is a multiple of 8.
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = gridDim.x >> 3;
+    const int i_lo = (int)((long)n_items * xcd / 8);
+    const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
+
+    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
         const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB);
         const int nb = item % NB;
-        const uint16_t* Wg =
-            tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
+        const uint16_t* Wg = tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
         int ra, rb;
         if (kSwiGLU) {
             ra = nb * 64 + 16 * wave + li;
@@ -157,14 +195,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             ra = nb * 128 + 32 * wave + li;
             rb = ra + 16;
         }
-        const uint16_t* wa = Wg + (size_t)ra * K + 32 * lk;
-        const uint16_t* wb = Wg + (size_t)rb * K + 32 * lk;
+        const u32x4* wa = reinterpret_cast<const u32x4*>(Wg + (size_t)ra * K + 8 * lk);
+        const u32x4* wb = reinterpret_cast<const u32x4*>(Wg + (size_t)rb * K + 8 * lk);
         const int nms = (tile.rows + 15) >> 4;
 
-        // activation staging: thread -> (row tr, 32-element quarter tq)
-        const int tr = threadIdx.x >> 2, tq = threadIdx.x & 3;
-        const bool xin = tr < tile.rows;
-        const uint16_t* xsrc = X + (size_t)(tile.row0 + (xin ? tr : 0)) * K + 32 * tq;
+        // activation staging: wave w owns tile rows [16w, 16w+16); lane (li, lk)
+        // copies 64 B of row 16w+li (k = 32c + 8lk pieces, c = 0..3)
+        const bool xown = 16 * wave < tile.rows;
+        const int xrow = 16 * wave + li;
+        const int xrr = xrow < tile.rows ? xrow : tile.rows - 1;
+        const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 8 * lk);
 
         f32x4 acc_a[4], acc_b[4];
 #pragma unroll
@@ -172,58 +212,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
             acc_a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc_b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        u32x4 ring[3][2][4];
+        u32x4 xr[4];
 
-        u32x4 wa_cur[4], wb_cur[4], wa_nxt[4], wb_nxt[4], xr[4];
+        auto load_w = [&](int kc, auto slot_c) {
+            constexpr int st = decltype(slot_c)::value;
+            kc = kc < nk ? kc : nk - 1;
+            const int ko = kc * (kBK / 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wa_cur[i] = reinterpret_cast<const u32x4*>(wa)[i];
-            wb_cur[i] = reinterpret_cast<const u32x4*>(wb)[i];
-            xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc)[i] : u32x4{0, 0, 0, 0};
-        }
-        {
-            u32x4* d = reinterpret_cast<u32x4*>(&xs[0][tr * kLdsRowBf16 + 64 * tq]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) d[i] = xr[i];
-        }
-        __syncthreads();
-
-        for (int kc = 0; kc < nk; ++kc) {
-            const int buf = kc & 1;
-            const bool more = kc + 1 < nk;
-            if (more) {
-                const int ko = (kc + 1) * kBK;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    wa_nxt[i] = reinterpret_cast<const u32x4*>(wa + ko)[i];
-                    wb_nxt[i] = reinterpret_cast<const u32x4*>(wb + ko)[i];
-                    xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc + ko)[i] : u32x4{0, 0, 0, 0};
-                }
+            for (int c = 0; c < 4; ++c) {
+                ring[st][0][c] = wa[ko + 4 * c];
+                ring[st][1][c] = wb[ko + 4 * c];
             }
+        };
+        auto load_x = [&](int kc) {
+            kc = kc < nk ? kc : nk - 1;
+            const int ko = kc * (kBK / 8);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xr[c] = xsrc[ko + 4 * c];
+        };
+        auto store_x = [&](int buf) {
+            if (xown) {
+                uint8_t* d = &xs[buf][xrow * kLdsRowBf16];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<u32x4*>(d + 64 * c + 16 * lk) = xr[c];
+            }
+        };
+        auto compute = [&](int buf, auto slot_c) {
+            constexpr int st = decltype(slot_c)::value;
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
                 if (ms < nms) {
-                    const u32x4* bp = reinterpret_cast<const u32x4*>(
-                        &xs[buf][(ms * 16 + li) * kLdsRowBf16 + 64 * lk]);
+                    const uint8_t* row = &xs[buf][(ms * 16 + li) * kLdsRowBf16 + 16 * lk];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const u32x4 b = bp[c];
-                        acc_a[ms] = mfma_bf16(wa_cur[c], b, acc_a[ms]);
-                        acc_b[ms] = mfma_bf16(wb_cur[c], b, acc_b[ms]);
+                        const u32x4 b = *reinterpret_cast<const u32x4*>(row + 64 * c);
+                        acc_a[ms] = mfma_bf16(ring[st][0][c], b, acc_a[ms]);
+                        acc_b[ms] = mfma_bf16(ring[st][1][c], b, acc_b[ms]);
                     }
                 }
             }
-            if (more) {
-                u32x4* d = reinterpret_cast<u32x4*>(&xs[buf ^ 1][tr * kLdsRowBf16 + 64 * tq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) d[i] = xr[i];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    wa_cur[i] = wa_nxt[i];
-                    wb_cur[i] = wb_nxt[i];
-                }
-            }
-            __syncthreads();
+        };
+        // one K step: activations of j+1 first, then weights of j+2, compute j,
+        // wait for the activations only, stage them, barrier
+        auto step = [&](int j, auto cur, auto nxt) {
+            load_x(j + 1);
+            load_w(j + 2, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(j & 1, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<8>();
+            store_x((j + 1) & 1);
+            barrier_only();
+        };
+
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        // prologue: activations of step 0 into LDS, weights of steps 0 and 1
+        load_x(0);
+        load_w(0, S0{});
+        load_w(1, S1{});
+        wait_vmcnt<16>();
+        store_x(0);
+        barrier_only();
+        for (int j = 0;; j += 3) {
+            step(j, S0{}, S2{});
+            if (j + 1 >= nk) break;
+            step(j + 1, S1{}, S0{});
+            if (j + 2 >= nk) break;
+            step(j + 2, S2{}, S1{});
+            if (j + 3 >= nk) break;
         }
+        wait_vmcnt<0>();  // the clamped tail loads land before registers are reused
 
         // epilogue: lane holds D[n = base + 4*lk + r][m = ms*16 + li]
 #pragma unroll
@@ -506,6 +568,12 @@ int persistent_grid(long bound, int per_cu) {
     return (int)(g > 0 ? g : 1);
 }
 
+// persistent grid rounded up to a multiple of the 8 XCDs
+int persistent_grid_xcd(long bound, int per_cu) {
+    const int g = persistent_grid(bound, per_cu);
+    return (g + 7) / 8 * 8;
+}
+
 }  // namespace
 
 size_t ffn_workspace_bytes(const moe_expert_weights* w, int max_rows) {
@@ -527,7 +595,7 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
     }
     if (w->dt == MOE_BF16) {
         const int NB = I / 64;
-        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<true>, dim3(persistent_grid(tiles_bound * NB, 3)),
+        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<true>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                            dim3(kThreads), 0, st, (const uint16_t*)x_perm, (const uint16_t*)w->w13,
                            (const uint16_t*)w->ws13, E, offsets, n_groups, max_rows, H, 2 * I, NB,
                            (uint16_t*)s.a, I);
@@ -555,7 +623,7 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
     }
     if (w->dt == MOE_BF16) {
         const int NB = H / 128;
-        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<false>, dim3(persistent_grid(tiles_bound * NB, 3)),
+        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<false>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                            dim3(kThreads), 0, st, (const uint16_t*)s.a, (const uint16_t*)w->w2,
                            (const uint16_t*)w->ws2, E, offsets, n_groups, max_rows, I, H, NB,
                            (uint16_t*)y_perm, H);
