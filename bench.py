@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--cpu-sample", type=int, default=16,
                     help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -294,6 +296,14 @@ def main():
                            "tflops": round(lflops / (ms / 1e3) / 1e12, 2)},
         "cpu_baseline": None,
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+        del src, dst
     if args.cpu_sample > 0:
         log(f"[bench] cpu oracle baseline on {args.cpu_sample} tokens")
         line["cpu_baseline"] = cpu_baseline(cfg, layer, b, x, st, sh, topk, args.cpu_sample)

@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB_PATH selects another build of the same library (A/B comparisons)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 SOFTMAX, SIGMOID = 0, 1

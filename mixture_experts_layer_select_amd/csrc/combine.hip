@@ -65,14 +65,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
         if (vec) {
             for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
                 float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                for (int j = 0; j < k; ++j) {
-                    const int r = rows[j];
-                    if (r < 0) continue;
-                    float v[8];
-                    load8(y + (size_t)r * H + h, v);
-                    const float wj = wts[j];
+                // picks in slot order, 8 at a time: all 8 row loads are issued
+                // before the first multiply-add so their latencies overlap
+                for (int j0 = 0; j0 < k; j0 += 8) {
+                    float v[8][8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+                    for (int q = 0; q < 8; ++q) {
+                        const int j = j0 + q;
+                        const int r = j < k ? rows[j] : -1;
+                        if (r >= 0) load8(y + (size_t)r * H + h, v[q]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int j = j0 + q;
+                        if (j < k && rows[j] >= 0) {
+                            const float wj = wts[j];
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[q][i], acc[i]);
+                        }
+                    }
                 }
                 if (rows[k] >= 0) {
                     float v[8];

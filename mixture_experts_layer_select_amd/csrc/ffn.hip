@@ -31,7 +31,12 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 64;      // rows per m-tile
+constexpr int kBM = 64;      // rows per m-tile (fp8 kernels)
+constexpr int kBigTile = 64;  // rows per m-tile of the bf16 kernels (128 measured slower)
+#ifndef MOE_BF16_OCC
+#define MOE_BF16_OCC 2
+#endif
+constexpr int kBf16Occ = MOE_BF16_OCC;  // waves per SIMD the bf16 GEMMs are compiled for
 constexpr int kBK = 128;     // K per step
 constexpr int kThreads = 256;
 
@@ -56,9 +61,10 @@ struct TileMap {
     int part[256];
 };
 
-// all threads of the block must call; returns the total number of tiles
+// all threads of the block must call; returns the total number of tiles of
+// bm rows
 __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int n_groups,
-                              int max_rows) {
+                              int max_rows, int bm) {
     const int per = (n_groups + 255) / 256;
     const int g0 = threadIdx.x * per;
     int local[5];  // per <= 5 since n_groups <= 1025 (+ slack)
@@ -69,7 +75,7 @@ __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, 
         int nt = 0;
         if (i < per && g < n_groups) {
             const int m = clamp_row(offsets[g + 1], max_rows) - clamp_row(offsets[g], max_rows);
-            nt = m > 0 ? (m + kBM - 1) / kBM : 0;
+            nt = m > 0 ? (m + bm - 1) / bm : 0;
         }
         local[i] = nt;
         sum += nt;
@@ -95,7 +101,7 @@ __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, 
 }
 
 __device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __restrict__ offsets,
-                                         int n_groups, int max_rows, int mt) {
+                                         int n_groups, int max_rows, int mt, int bm) {
     int lo = 0, hi = n_groups - 1;  // last g with start[g] <= mt
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -106,8 +112,8 @@ __device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __res
     t.group = lo;
     const int r0 = clamp_row(offsets[lo], max_rows);
     const int r1 = clamp_row(offsets[lo + 1], max_rows);
-    t.row0 = r0 + (mt - tm.start[lo]) * kBM;
-    t.rows = min(kBM, r1 - t.row0);
+    t.row0 = r0 + (mt - tm.start[lo]) * bm;
+    t.rows = min(bm, r1 - t.row0);
     return t;
 }
 
@@ -159,12 +165,14 @@ __device__ __forceinline__ void barrier_only() {
     __builtin_amdgcn_s_barrier();
 }
 
-template <bool kSwiGLU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gemm_bf16_kernel(
+template <bool kSwiGLU, int kTM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16Occ, kBf16Occ))) void ffn_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ws,
     int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
     int NB, uint16_t* __restrict__ out, int ldo) {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kBM * kLdsRowBf16];
+    constexpr int kSub = kTM / 16;    // m-subtiles per tile
+    constexpr int kOwn = kTM / 64;    // 16-row pieces of the tile each wave stages
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kTM * kLdsRowBf16];
     __shared__ TileMap tm;
 
     const int lane = threadIdx.x & 63;
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int nk = K / kBK;
-    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows) * NB;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kTM) * NB;
 
     // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin
     // (blockIdx % 8); each XCD walks a contiguous slice of the items, so the
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
 
     for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
-        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB);
+        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kTM);
         const int nb = item % NB;
         const uint16_t* Wg = tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
         int ra, rb;
@@ -199,21 +207,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const u32x4* wb = reinterpret_cast<const u32x4*>(Wg + (size_t)rb * K + 8 * lk);
         const int nms = (tile.rows + 15) >> 4;
 
-        // activation staging: wave w owns tile rows [16w, 16w+16); lane (li, lk)
-        // copies 64 B of row 16w+li (k = 32c + 8lk pieces, c = 0..3)
-        const bool xown = 16 * wave < tile.rows;
-        const int xrow = 16 * wave + li;
-        const int xrr = xrow < tile.rows ? xrow : tile.rows - 1;
-        const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 8 * lk);
-
-        f32x4 acc_a[4], acc_b[4];
+        // activation staging: wave w owns tile rows 16(w + 4q) + [0, 16), q < kOwn;
+        // lane (li, lk) copies 64 B of each such row (k = 32c + 8lk pieces)
+        bool xown[kOwn];
+        int xrow[kOwn];
+        const u32x4* xsrc[kOwn];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int q = 0; q < kOwn; ++q) {
+            const int base = 16 * (wave + 4 * q);
+            xown[q] = base < tile.rows;
+            xrow[q] = base + li;
+            const int xrr = xrow[q] < tile.rows ? xrow[q] : tile.rows - 1;
+            xsrc[q] = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 8 * lk);
+        }
+
+        f32x4 acc_a[kSub], acc_b[kSub];
+#pragma unroll
+        for (int i = 0; i < kSub; ++i) {
             acc_a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc_b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         u32x4 ring[3][2][4];
-        u32x4 xr[4];
+        u32x4 xr[kOwn][4];
 
         auto load_w = [&](int kc, auto slot_c) {
             constexpr int st = decltype(slot_c)::value;
@@ -229,20 +244,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             kc = kc < nk ? kc : nk - 1;
             const int ko = kc * (kBK / 8);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) xr[c] = xsrc[ko + 4 * c];
+            for (int q = 0; q < kOwn; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xr[q][c] = xsrc[q][ko + 4 * c];
         };
         auto store_x = [&](int buf) {
-            if (xown) {
-                uint8_t* d = &xs[buf][xrow * kLdsRowBf16];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    *reinterpret_cast<u32x4*>(d + 64 * c + 16 * lk) = xr[c];
+            for (int q = 0; q < kOwn; ++q) {
+                if (xown[q]) {
+                    uint8_t* d = &xs[buf][xrow[q] * kLdsRowBf16];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        *reinterpret_cast<u32x4*>(d + 64 * c + 16 * lk) = xr[q][c];
+                }
             }
         };
         auto compute = [&](int buf, auto slot_c) {
             constexpr int st = decltype(slot_c)::value;
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
+            for (int ms = 0; ms < kSub; ++ms) {
                 if (ms < nms) {
                     const uint8_t* row = &xs[buf][(ms * 16 + li) * kLdsRowBf16 + 16 * lk];
 #pragma unroll
@@ -255,7 +275,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         };
         // one K step: activations of j+1 first, then weights of j+2, compute j,
-        // wait for the activations only, stage them, barrier
+        // wait for the activations only (the 8 weight loads stay in flight),
+        // stage them, barrier
         auto step = [&](int j, auto cur, auto nxt) {
             load_x(j + 1);
             load_w(j + 2, nxt);
@@ -266,6 +287,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             store_x((j + 1) & 1);
             barrier_only();
         };
+        static_assert(kOwn * 4 + 16 < 64, "prologue wait count");
 
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
@@ -274,7 +296,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         load_x(0);
         load_w(0, S0{});
         load_w(1, S1{});
-        wait_vmcnt<16>();
+        wait_vmcnt<16>();  // the activations of step 0 (issued first) have landed
         store_x(0);
         barrier_only();
         for (int j = 0;; j += 3) {
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         // epilogue: lane holds D[n = base + 4*lk + r][m = ms*16 + li]
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
+        for (int ms = 0; ms < kSub; ++ms) {
             const int m = ms * 16 + li;
             if (ms < nms && m < tile.rows) {
                 uint16_t* orow = out + (size_t)(tile.row0 + m) * ldo;
@@ -339,11 +361,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int nk = K / kBK;
-    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows) * NB;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kBM) * NB;
     const int kbn = K / kBK;  // scale blocks along K
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB);
+        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kBM);
         const int nb = item % NB;
         const bool routed = tile.group < n_routed;
         const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
@@ -595,7 +617,8 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
     }
     if (w->dt == MOE_BF16) {
         const int NB = I / 64;
-        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<true>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
+        const long tiles128 = (long)(max_rows + kBigTile - 1) / kBigTile + n_groups;
+        hipLaunchKernelGGL((ffn_gemm_bf16_kernel<true, kBigTile>), dim3(persistent_grid_xcd(tiles128 * NB, kBf16Occ)),
                            dim3(kThreads), 0, st, (const uint16_t*)x_perm, (const uint16_t*)w->w13,
                            (const uint16_t*)w->ws13, E, offsets, n_groups, max_rows, H, 2 * I, NB,
                            (uint16_t*)s.a, I);
@@ -623,7 +646,8 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
     }
     if (w->dt == MOE_BF16) {
         const int NB = H / 128;
-        hipLaunchKernelGGL(ffn_gemm_bf16_kernel<false>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
+        const long tiles128 = (long)(max_rows + kBigTile - 1) / kBigTile + n_groups;
+        hipLaunchKernelGGL((ffn_gemm_bf16_kernel<false, kBigTile>), dim3(persistent_grid_xcd(tiles128 * NB, kBf16Occ)),
                            dim3(kThreads), 0, st, (const uint16_t*)s.a, (const uint16_t*)w->w2,
                            (const uint16_t*)w->ws2, E, offsets, n_groups, max_rows, I, H, NB,
                            (uint16_t*)y_perm, H);

@@ -133,6 +133,75 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
     }
 }
 
+// All of hist + scan + scatter + fill in one workgroup of 1024 threads when
+// the slots fit one LDS bitmap: per local expert a bitmap over all slots
+// (nw = ceil(S/32) words), 16-bit popcount prefixes per word, an exclusive
+// scan over experts. Used when S <= kSmallSlots and the bitmap fits kSmallLds.
+constexpr int kSmallSlots = 8192;
+constexpr size_t kSmallLds = 96 * 1024;
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restrict__ ids, int S,
+                                                          int T, int base, int E_local,
+                                                          int n_shared, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ row_to_slot,
+                                                          int32_t* __restrict__ slot_to_row) {
+    const int nw = (S + 31) / 32;
+    const int kWords = nw;  // row stride of both tables
+    extern __shared__ uint32_t smem[];
+    uint32_t* bits = smem;                                              // [E_local][nw]
+    uint16_t* pre = reinterpret_cast<uint16_t*>(smem + E_local * nw);  // [E_local][nw]
+    __shared__ int excl[kMaxLocal + 2];
+    for (int i = threadIdx.x; i < E_local * kWords; i += blockDim.x) bits[i] = 0;
+    __syncthreads();
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        const int e = ids[s] - base;
+        if (e >= 0 && e < E_local) atomicOr(&bits[e * kWords + (s >> 5)], 1u << (s & 31));
+    }
+    __syncthreads();
+    if (threadIdx.x < E_local) {
+        const int e = threadIdx.x;
+        int run = 0;
+        for (int w = 0; w < nw; ++w) {
+            pre[e * kWords + w] = (uint16_t)run;
+            run += __popc(bits[e * kWords + w]);
+        }
+        excl[e] = run;  // count for now
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int g = 0; g < E_local; ++g) {
+            const int c = excl[g];
+            counts[g] = c;
+            offsets[g] = run;
+            excl[g] = run;
+            run += c;
+        }
+        counts[E_local] = n_shared;
+        offsets[E_local] = run;
+        offsets[E_local + 1] = run + n_shared;
+        excl[E_local] = run;
+    }
+    __syncthreads();
+    const int R = excl[E_local];
+    for (int s = threadIdx.x; s < S; s += blockDim.x) {
+        const int e = ids[s] - base;
+        if (e >= 0 && e < E_local) {
+            const int w = s >> 5;
+            const int row = excl[e] + pre[e * kWords + w] +
+                            __popc(bits[e * kWords + w] & ((1u << (s & 31)) - 1u));
+            row_to_slot[row] = s;
+            slot_to_row[s] = row;
+        } else {
+            slot_to_row[s] = -1;
+        }
+    }
+    const int cap = S + T;
+    for (int r = R + threadIdx.x; r < cap; r += blockDim.x)
+        row_to_slot[r] = r < R + n_shared ? S + (r - R) : -1;
+}
+
 __global__ void perm_fill_kernel(const int32_t* __restrict__ offsets, int E_local, long S,
                                  long cap, int32_t* __restrict__ row_to_slot) {
     const long R = offsets[E_local];
@@ -206,6 +275,11 @@ __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
 
 }  // namespace
 
+static moe_status launch_gather(const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt,
+                                const int32_t* row_to_slot, const int32_t* offsets, int E_local,
+                                long S, int k, long cap, void* x_perm, float* x_perm_scale,
+                                hipStream_t st);
+
 size_t permute_workspace_bytes(int T, int k, int E_local) {
     long S = (long)T * k;
     long n_chunks = (S + kChunk - 1) / kChunk;
@@ -220,10 +294,26 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_loca
     const long cap = S + T;
     const int n_chunks = (int)((S + kChunk - 1) / kChunk);
     int32_t* chunk_counts = (int32_t*)ws;
+    moe_status s;
+    const size_t small_lds = (size_t)E_local * ((S + 31) / 32) * (4 + 2);
+    if (S <= kSmallSlots && small_lds <= kSmallLds) {
+        const size_t smem = small_lds;
+        static bool lds_opt_in = [] {  // dynamic LDS above 64 KB needs the attribute
+            return hipFuncSetAttribute((const void*)perm_small_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kSmallLds) == hipSuccess;
+        }();
+        if (!lds_opt_in) return set_error(MOE_ERR_HIP, "perm_small_kernel: LDS attribute refused");
+        hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), smem, st, ids, (int)S, T, base,
+                           E_local, include_shared ? T : 0, counts, offsets, row_to_slot,
+                           slot_to_row);
+        if ((s = check_launch("perm_small_kernel"))) return s;
+        return launch_gather(x, x_dt, H, perm_dt, row_to_slot, offsets, E_local, S, k, cap,
+                             x_perm, x_perm_scale, st);
+    }
     hipLaunchKernelGGL(perm_hist_kernel, dim3(n_chunks), dim3(256), 0, st, ids, S, base, E_local,
                        chunk_counts);
-    moe_status s = check_launch("perm_hist_kernel");
-    if (s) return s;
+    if ((s = check_launch("perm_hist_kernel"))) return s;
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, st, chunk_counts, n_chunks, E_local,
                        include_shared ? T : 0, counts, offsets);
     if ((s = check_launch("perm_scan_kernel"))) return s;
@@ -234,6 +324,14 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_loca
     hipLaunchKernelGGL(perm_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, offsets, E_local, S, cap,
                        row_to_slot);
     if ((s = check_launch("perm_fill_kernel"))) return s;
+    return launch_gather(x, x_dt, H, perm_dt, row_to_slot, offsets, E_local, S, k, cap, x_perm,
+                         x_perm_scale, st);
+}
+
+static moe_status launch_gather(const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt,
+                                const int32_t* row_to_slot, const int32_t* offsets, int E_local,
+                                long S, int k, long cap, void* x_perm, float* x_perm_scale,
+                                hipStream_t st) {
     if (!x_perm) return MOE_OK;
     const int cu = device_info().cu_count;
     const int gather_blocks = (int)std::min<long>(cap, (long)cu * 8);

@@ -2,16 +2,14 @@
 // combine weights ([Moreh-EP] Overview: a lightweight gating network picks a
 // small subset of experts per token; Parallelization: top-8 of 256 for R1).
 //
-// Logits. A wavefront of 64 lanes owns a 4-token x 16-expert tile of (t, e)
+// Logits. A wavefront of 64 lanes owns an 8-token x 8-expert tile of (t, e)
 // pairs. Lane j accumulates, for all 64 pairs, the 8-element chunks of h with
 // floor(h/8) mod 64 == j in ascending h with fused multiply-adds -- the same
 // lane/partial assignment the reduction order is defined by. The partials are
 // then combined pairwise (p[j] += p[j+s], s = 32..1) by a transposing
 // butterfly: at every level each lane hands half of its pairs to its partner,
 // so after 6 levels lane l holds the finished logit of pair l (63 exchanges
-// instead of 6 per pair). Tiles of x and w_router for one 512-wide h step
-// are staged in LDS and shared by the 4 waves of a workgroup (16 tokens x 16
-// experts per workgroup).
+// instead of 6 per pair).
 //
 // Selection. One wavefront per token, up to 4 logits per lane; k rounds of a
 // wave-wide maximum over a 64-bit key (order-preserving logit bits, then the
@@ -22,135 +20,136 @@
 namespace moe {
 namespace {
 
-constexpr int kTokTile = 16;   // tokens per workgroup (4 per wave)
-constexpr int kExpTile = 16;   // experts per workgroup
-constexpr int kStep = 512;     // h per step: 64 lanes x 8
+constexpr int kWT = 8;        // tokens per wave
+constexpr int kWE = 8;        // experts per wave
+constexpr int kStep = 512;    // h per step: 64 lanes x 8
 
+// 8 consecutive inputs as fp32 (zeros past H)
 template <typename TIn>
-struct RouteIO;
+struct Chunk;
 
 template <>
-struct RouteIO<uint16_t> {  // bf16 bit patterns
-    static constexpr int kBytes = 2;
-    // load the 8-element chunk [h0, h0+8) of a row, zero beyond H
-    static __device__ __forceinline__ void load8(const uint16_t* row, int h0, int H, float* v) {
-        if (h0 + 8 <= H && (H & 7) == 0) {
-            u32x4 q = *reinterpret_cast<const u32x4*>(row + h0);
+struct Chunk<uint16_t> {  // bf16 bit patterns: 8 values in one 16-byte load
+    u32x4 raw;
+    __device__ __forceinline__ void load(const uint16_t* row, int h0, int H, bool vec) {
+        if (vec && h0 + 8 <= H) {
+            raw = *reinterpret_cast<const u32x4*>(row + h0);
+        } else {
+            uint32_t v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                v[2 * i] = bf16_lo(q[i]);
-                v[2 * i + 1] = bf16_hi(q[i]);
+                uint32_t lo = h0 + 2 * i < H ? row[h0 + 2 * i] : 0u;
+                uint32_t hi = h0 + 2 * i + 1 < H ? row[h0 + 2 * i + 1] : 0u;
+                v[i] = lo | (hi << 16);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (h0 + i < H) ? bf16_to_f32(row[h0 + i]) : 0.0f;
+            raw = u32x4{v[0], v[1], v[2], v[3]};
         }
+    }
+    __device__ __forceinline__ float at(int i) const {
+        return (i & 1) ? bf16_hi(raw[i >> 1]) : bf16_lo(raw[i >> 1]);
     }
 };
 
 template <>
-struct RouteIO<float> {
-    static constexpr int kBytes = 4;
-    static __device__ __forceinline__ void load8(const float* row, int h0, int H, float* v) {
-        if (h0 + 8 <= H && (H & 3) == 0) {
-            f32x4 a = *reinterpret_cast<const f32x4*>(row + h0);
-            f32x4 b = *reinterpret_cast<const f32x4*>(row + h0 + 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[i] = a[i];
-                v[4 + i] = b[i];
-            }
+struct Chunk<float> {
+    f32x4 lo, hi;
+    __device__ __forceinline__ void load(const float* row, int h0, int H, bool vec) {
+        if (vec && h0 + 8 <= H) {
+            lo = *reinterpret_cast<const f32x4*>(row + h0);
+            hi = *reinterpret_cast<const f32x4*>(row + h0 + 4);
         } else {
+            float v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (h0 + i < H) ? row[h0 + i] : 0.0f;
+            for (int i = 0; i < 8; ++i) v[i] = h0 + i < H ? row[h0 + i] : 0.0f;
+            lo = f32x4{v[0], v[1], v[2], v[3]};
+            hi = f32x4{v[4], v[5], v[6], v[7]};
         }
     }
+    __device__ __forceinline__ float at(int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
 };
 
-// LDS tile: rows of 512 elements stored as fp32 (converted once while
-// staging). Element 8j + 4q + i of a row (chunk j, half q) sits at
-// [q*256 + 4j + i], so the 64 lanes of a wave read two contiguous 1 KB runs.
+// A wave owns 8 tokens x 8 experts = 64 (t, e) pairs; a workgroup of 4 waves
+// covers 8 tokens x 32 experts. Lane j reads its 16-byte chunk of each of the
+// 16 rows straight from global memory (a wave reads 1 KB contiguous per row
+// and step), one step ahead in registers; no LDS. Every input row is read
+// whole by every wave that needs it, so reuse happens in L2. Rows past T or E
+// read a valid row; those pairs are never written. Zero padding past H adds
+// fma(0, 0, p) = p exactly (a partial that starts at +0 is never -0).
+// Vector loads need H % 8 == 0 (bf16) / H % 4 == 0 (fp32) for alignment;
+// other H take the element path for every chunk.
 template <typename TIn>
 __global__ __launch_bounds__(256) void route_logits_kernel(const TIn* __restrict__ x,
                                                            const TIn* __restrict__ w,
                                                            const float* __restrict__ bias, int T,
                                                            int H, int E,
                                                            float* __restrict__ logits) {
-    __shared__ float xs[kTokTile][kStep];
-    __shared__ float ws[kExpTile][kStep];
-
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kTokTile;
-    const int e0 = blockIdx.y * kExpTile;
+    const int t0 = blockIdx.x * kWT;
+    const int e0 = (blockIdx.y * 4 + wave) * kWE;
+    const bool aligned = sizeof(TIn) == 2 ? (H & 7) == 0 : (H & 3) == 0;
 
-    float acc[4][kExpTile];
+    const TIn* xr[kWT];
+    const TIn* wr[kWE];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kWT; ++a) xr[a] = x + (size_t)min(t0 + a, T - 1) * H;
 #pragma unroll
-        for (int b = 0; b < kExpTile; ++b) acc[a][b] = 0.0f;
+    for (int b = 0; b < kWE; ++b) wr[b] = w + (size_t)min(e0 + b, E - 1) * H;
 
-    for (int hs = 0; hs < H; hs += kStep) {
-        // stage: 32 rows x 64 chunks of 8; thread i loads chunks i, i+256, ...
-        for (int c = threadIdx.x; c < (kTokTile + kExpTile) * 64; c += 256) {
-            int r = c >> 6, j = c & 63;
-            float v[8];
-            int h0 = hs + 8 * j;
-            if (r < kTokTile) {
-                int t = t0 + r;
-                if (t < T) RouteIO<TIn>::load8(x + (size_t)t * H, h0, H, v);
-                else
+    float acc[kWT][kWE];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int a = 0; a < kWT; ++a)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xs[r][4 * j + i] = v[i];
-                    xs[r][256 + 4 * j + i] = v[4 + i];
-                }
-            } else {
-                int e = e0 + r - kTokTile;
-                if (e < E) RouteIO<TIn>::load8(w + (size_t)e * H, h0, H, v);
-                else
+        for (int b = 0; b < kWE; ++b) acc[a][b] = 0.0f;
+
+    Chunk<TIn> cx[2][kWT], cw[2][kWE];
+    auto load = [&](int buf, int hs) {
+        const int h0 = hs + 8 * lane;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        for (int a = 0; a < kWT; ++a) cx[buf][a].load(xr[a], h0, H, aligned);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ws[r - kTokTile][4 * j + i] = v[i];
-                    ws[r - kTokTile][256 + 4 * j + i] = v[4 + i];
-                }
-            }
+        for (int b = 0; b < kWE; ++b) cw[buf][b].load(wr[b], h0, H, aligned);
+    };
+    auto fma_step = [&](int buf) {
+        // partial of lane j, ascending h inside its chunk, every pair
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float xv[kWT], wv[kWE];
+#pragma unroll
+            for (int a = 0; a < kWT; ++a) xv[a] = cx[buf][a].at(i);
+#pragma unroll
+            for (int b = 0; b < kWE; ++b) wv[b] = cw[buf][b].at(i);
+#pragma unroll
+            for (int a = 0; a < kWT; ++a)
+#pragma unroll
+                for (int b = 0; b < kWE; ++b) acc[a][b] = __builtin_fmaf(xv[a], wv[b], acc[a][b]);
         }
-        __syncthreads();
-        float xv[4][8];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            f32x4 lo = *reinterpret_cast<const f32x4*>(&xs[wave * 4 + a][4 * lane]);
-            f32x4 hi = *reinterpret_cast<const f32x4*>(&xs[wave * 4 + a][256 + 4 * lane]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xv[a][i] = lo[i];
-                xv[a][4 + i] = hi[i];
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < kExpTile; ++b) {
-            f32x4 lo = *reinterpret_cast<const f32x4*>(&ws[b][4 * lane]);
-            f32x4 hi = *reinterpret_cast<const f32x4*>(&ws[b][256 + 4 * lane]);
-            float wv[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int a = 0; a < 4; ++a) acc[a][b] = __builtin_fmaf(xv[a][i], wv[i], acc[a][b]);
-        }
-        __syncthreads();
+    };
+    load(0, 0);
+    int hs = 0;
+    for (;;) {
+        const bool more = hs + kStep < H;
+        if (more) load(1, hs + kStep);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_step(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!more) break;
+        hs += kStep;
+        const bool more2 = hs + kStep < H;
+        if (more2) load(0, hs + kStep);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_step(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!more2) break;
+        hs += kStep;
     }
 
-    // transposing pairwise reduction: pair p = a*16 + b ends in lane p
+    // transposing pairwise reduction: pair p = a*8 + b ends in lane p
     float v[64];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kWT; ++a)
 #pragma unroll
-        for (int b = 0; b < kExpTile; ++b) v[a * kExpTile + b] = acc[a][b];
+        for (int b = 0; b < kWE; ++b) v[a * kWE + b] = acc[a][b];
 #pragma unroll
     for (int s = 32, n = 64; s >= 1; s >>= 1, n >>= 1) {
         const bool hi = (lane & s) != 0;
@@ -162,8 +161,8 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const TIn* __restrict
             v[i] = keep + got;
         }
     }
-    const int t = t0 + wave * 4 + (lane >> 4);
-    const int e = e0 + (lane & 15);
+    const int t = t0 + (lane >> 3);
+    const int e = e0 + (lane & 7);
     if (t < T && e < E) {
         float l = v[0];
         if (bias) l = l + bias[e];
@@ -269,7 +268,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 moe_status launch_route(const void* x, const void* w, const float* bias, moe_dtype dt, int T, int H,
                         int E, int k, int scoring, int renorm, float* logits, int32_t* ids,
                         float* topk_w, hipStream_t st) {
-    dim3 grid((T + kTokTile - 1) / kTokTile, (E + kExpTile - 1) / kExpTile);
+    dim3 grid((T + kWT - 1) / kWT, (E + 4 * kWE - 1) / (4 * kWE));
     if (dt == MOE_BF16)
         hipLaunchKernelGGL(route_logits_kernel<uint16_t>, grid, dim3(256), 0, st,
                            (const uint16_t*)x, (const uint16_t*)w, bias, T, H, E, logits);
