@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
-    ap.add_argument("--cpu-sample", type=int, default=16,
+    ap.add_argument("--cpu-sample", type=int, default=256,
                     help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
@@ -168,6 +168,29 @@ def layer_alg(cfg, layer, counts, T, n_rows):
     return byt, flops
 
 
+def profiled_traffic(kernel_key: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    and workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
+    size), or None when there is none or the kernel source changed since."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "mixture_experts_layer_select_amd", "csrc", "ffn.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            line = line.strip()
+            if not (line.startswith("{") and "traffic_bytes" in line):
+                continue
+            try:
+                rec = json.loads(line)
+            except ValueError:
+                continue
+            if (rec.get("kernel") == kernel_key and rec.get("workload") == workload
+                    and rec.get("ffn_hip_sha256") == digest):
+                return int(rec["traffic_bytes"])
+    return None
+
+
 def cpu_groups(st, sh, ids, base, E_local):
     """Host copies of the experts that the sampled tokens pick (+ shared)."""
     used = sorted({int(e) - base for e in ids.ravel() if 0 <= int(e) - base < E_local})
@@ -287,7 +310,8 @@ def main():
                    "rows": n_rows, **info},
         "roofline": {"kernel": f"ffn_gemm_{fmt_key}_kernel<gate_up>", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(f"gemm_{fmt_key}_kernel<true", f"c{cfg.cid}"),
                      "bytes_per_launch": int(gbytes), "avg_launch_ms": round(k_ms, 4)},
         "layer_roofline": {"bytes": int(lbytes), "flops": lflops,
                            "t_roof_ms": round(t_roof * 1e3, 4),

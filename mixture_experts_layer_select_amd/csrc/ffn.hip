@@ -109,11 +109,13 @@ __device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __res
         else hi = mid - 1;
     }
     MTile t;
-    t.group = lo;
     const int r0 = clamp_row(offsets[lo], max_rows);
     const int r1 = clamp_row(offsets[lo + 1], max_rows);
-    t.row0 = r0 + (mt - tm.start[lo]) * bm;
-    t.rows = min(bm, r1 - t.row0);
+    const int row0 = r0 + (mt - tm.start[lo]) * bm;
+    // the same for every lane: keep it in scalar registers
+    t.group = __builtin_amdgcn_readfirstlane(lo);
+    t.row0 = __builtin_amdgcn_readfirstlane(row0);
+    t.rows = __builtin_amdgcn_readfirstlane(min(bm, r1 - row0));
     return t;
 }
 
@@ -339,11 +341,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
 
 // ============================================================================ fp8
 // SwiGLU (GEMM-1): an item covers 128 intermediate columns = one 1x128 output
-//   quantisation block; wave w owns gate rows n0+32w+{0,16}+li and the up rows
-//   I + the same (n0 = nb*128). Output: A codes [rows][I] + scales [rows][I/128].
+//   quantisation block; wave w owns gate rows n0+32w+16h+li (h = 0, 1) and the
+//   up rows I + the same (n0 = nb*128). Output: A codes [rows][I] + scales
+//   [rows][I/128].
 // Down (GEMM-2): an item covers 256 output columns; wave w owns rows
 //   n0+64w+16s+li, s = 0..3 (n0 = nb*256). Output: y [rows][H] bf16.
-constexpr int kLdsRowFp8 = kBK + 16;  // bytes per staged activation row
+//
+// Same pipeline as the bf16 kernel: the activation codes (and their 1x128
+// scales) of step j+1 are loaded first and staged through LDS, the weight
+// codes of step j+2 go into a 3-deep register ring, and the weight block
+// scales of step j+2 into a small ring of wave-uniform registers. One K step
+// is one 128x128 weight block: MFMA 16x16x128 with unit E8M0 scales gives
+// the block's partial product, which is multiplied by (weight scale x
+// activation scale) and added to the fp32 accumulator. Lane (li, lk) holds
+// the 32 codes at bytes 16lk + [0,16) and 64 + 16lk + [0,16) of its row's
+// 128-byte step, for weights and activations alike.
+constexpr int kLdsRowFp8 = kBK + 16;  // bytes per staged activation row (16 B pad)
 
 template <bool kSwiGLU>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gemm_fp8_kernel(
@@ -360,103 +373,132 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int wave = threadIdx.x >> 6;
     const int li = lane & 15;
     const int lk = lane >> 4;
-    const int nk = K / kBK;
+    const int nk = K / kBK;   // K steps = scale blocks along K
     const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kBM) * NB;
-    const int kbn = K / kBK;  // scale blocks along K
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int xcd = blockIdx.x & 7;  // XCD-contiguous slices of the items
+    const int per_xcd = gridDim.x >> 3;
+    const int i_lo = (int)((long)n_items * xcd / 8);
+    const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
+
+    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
         const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kBM);
         const int nb = item % NB;
         const bool routed = tile.group < n_routed;
         const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
-        const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * kbn : Wsh_sc;
-        int row[4];
+        const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
+        int rbase[4];  // first weight row of each 16-row subtile
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (kSwiGLU) row[s] = nb * 128 + 32 * wave + 16 * (s & 1) + li + (s >> 1) * (Nw / 2);
-            else row[s] = nb * 256 + 64 * wave + 16 * s + li;
+            if (kSwiGLU) rbase[s] = nb * 128 + 32 * wave + 16 * (s & 1) + (s >> 1) * (Nw / 2);
+            else rbase[s] = nb * 256 + 64 * wave + 16 * s;
         }
-        const uint8_t* wp[4];
+        const u32x4* wp[4];
+        const float* sp[4];  // scale row of each subtile's 128-row block (wave-uniform)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) wp[s] = Wg + (size_t)row[s] * K + 32 * lk;
-        // scale row block of each subtile (all 16 rows share one 128-row block)
-        int sblk[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) sblk[s] = (row[s] - li) / kBK;
+        for (int s = 0; s < 4; ++s) {
+            wp[s] = reinterpret_cast<const u32x4*>(Wg + (size_t)(rbase[s] + li) * K + 16 * lk);
+            sp[s] = Sg + (size_t)(rbase[s] / kBK) * nk;
+        }
         const int nms = (tile.rows + 15) >> 4;
 
-        // staging: thread -> (row tr, 32-byte quarter tq)
-        const int tr = threadIdx.x >> 2, tq = threadIdx.x & 3;
-        const bool xin = tr < tile.rows;
-        const uint8_t* xsrc = X + (size_t)(tile.row0 + (xin ? tr : 0)) * K + 32 * tq;
-        const float* ssrc = Xs + (size_t)(tile.row0 + (xin ? tr : 0)) * kbn;
+        // activation staging: wave w owns tile row 16w + li
+        const bool xown = 16 * wave < tile.rows;
+        const int xrow = 16 * wave + li;
+        const int xrr = xrow < tile.rows ? xrow : tile.rows - 1;
+        const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 16 * lk);
+        const float* ssrc = Xs + (size_t)(tile.row0 + xrr) * nk;
 
         f32x4 acc[4][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        i32x8 w_cur[4], w_nxt[4];
+        u32x8 ring[3][4];
+        float ring_sw[3][4];
         u32x4 xr[2];
-        float xsr = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) w_cur[s] = *reinterpret_cast<const i32x8*>(wp[s]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc)[i] : u32x4{0, 0, 0, 0};
-        if (tq == 0) xsr = xin ? ssrc[0] : 0.f;
-        {
-            u32x4* d = reinterpret_cast<u32x4*>(&xs[0][tr * kLdsRowFp8 + 32 * tq]);
-            d[0] = xr[0];
-            d[1] = xr[1];
-            if (tq == 0) xsc[0][tr] = xsr;
-        }
-        __syncthreads();
+        float xsr;
 
-        for (int kc = 0; kc < nk; ++kc) {
-            const int buf = kc & 1;
-            const bool more = kc + 1 < nk;
-            if (more) {
-                const int ko = (kc + 1) * kBK;
+        auto load_w = [&](int kc, auto slot_c) {
+            constexpr int st = decltype(slot_c)::value;
+            kc = kc < nk ? kc : nk - 1;
+            const int ko = kc * (kBK / 16);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) w_nxt[s] = *reinterpret_cast<const i32x8*>(wp[s] + ko);
+            for (int s = 0; s < 4; ++s)
+                ring[st][s] = __builtin_shufflevector(wp[s][ko], wp[s][ko + 4], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    xr[i] = xin ? reinterpret_cast<const u32x4*>(xsrc + ko)[i] : u32x4{0, 0, 0, 0};
-                if (tq == 0) xsr = xin ? ssrc[kc + 1] : 0.f;
+            for (int s = 0; s < 4; ++s) ring_sw[st][s] = sp[s][kc];
+        };
+        auto load_x = [&](int kc) {
+            kc = kc < nk ? kc : nk - 1;
+            const int ko = kc * (kBK / 16);
+            xr[0] = xsrc[ko];
+            xr[1] = xsrc[ko + 4];
+            xsr = ssrc[kc];
+        };
+        auto store_x = [&](int buf) {
+            if (xown) {
+                uint8_t* d = &xs[buf][xrow * kLdsRowFp8 + 16 * lk];
+                *reinterpret_cast<u32x4*>(d) = xr[0];
+                *reinterpret_cast<u32x4*>(d + 64) = xr[1];
+                if (lk == 0) xsc[buf][xrow] = xsr;
             }
-            float sw[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) sw[s] = Sg[(size_t)sblk[s] * kbn + kc];
+        };
+        auto compute = [&](int buf, auto slot_c) {
+            constexpr int st = decltype(slot_c)::value;
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
                 if (ms < nms) {
-                    const i32x8 b = *reinterpret_cast<const i32x8*>(
-                        &xs[buf][(ms * 16 + li) * kLdsRowFp8 + 32 * lk]);
-                    const float sx = xsc[buf][ms * 16 + li];
+                    const int m = ms * 16 + li;
+                    const uint8_t* row = &xs[buf][m * kLdsRowFp8 + 16 * lk];
+                    const u32x8 b = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(row),
+                                                            *reinterpret_cast<const u32x4*>(row + 64),
+                                                            0, 1, 2, 3, 4, 5, 6, 7);
+                    const float sx = xsc[buf][m];
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        const f32x4 p = mfma_fp8(w_cur[s], b);
-                        const float f = sw[s] * sx;
+                        const f32x4 p = mfma_fp8(__builtin_bit_cast(i32x8, ring[st][s]),
+                                                 __builtin_bit_cast(i32x8, b));
+                        const float f = ring_sw[st][s] * sx;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[s][ms][r] = __builtin_fmaf(p[r], f, acc[s][ms][r]);
                     }
                 }
             }
-            if (more) {
-                u32x4* d = reinterpret_cast<u32x4*>(&xs[buf ^ 1][tr * kLdsRowFp8 + 32 * tq]);
-                d[0] = xr[0];
-                d[1] = xr[1];
-                if (tq == 0) xsc[buf ^ 1][tr] = xsr;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) w_cur[s] = w_nxt[s];
-            }
-            __syncthreads();
+        };
+        // activations (2 + 1 loads) first, then weights (8 + 4 scale loads):
+        // waiting until only the 12 weight-side loads remain means the
+        // activations have landed
+        auto step = [&](int j, auto cur, auto nxt) {
+            load_x(j + 1);
+            load_w(j + 2, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(j & 1, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<12>();
+            store_x((j + 1) & 1);
+            barrier_only();
+        };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
+        load_x(0);
+        load_w(0, S0{});
+        load_w(1, S1{});
+        wait_vmcnt<24>();
+        store_x(0);
+        barrier_only();
+        for (int j = 0;; j += 3) {
+            step(j, S0{}, S2{});
+            if (j + 1 >= nk) break;
+            step(j + 1, S1{}, S0{});
+            if (j + 2 >= nk) break;
+            step(j + 2, S2{}, S1{});
+            if (j + 3 >= nk) break;
         }
+        wait_vmcnt<0>();
 
-        // epilogue: lane holds D[n = row base + 4*lk + r][m = ms*16 + li]
-        //   NOTE the accumulator rows are n = (row[s] - li) + 4*lk + r.
+        // epilogue: lane holds D[n = rbase[s] + 4*lk + r][m = ms*16 + li]
         if (kSwiGLU) {
             float a[2][4][4];  // [gate subtile][ms][r]
             float amax[4];
@@ -625,7 +667,7 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
         return check_launch("ffn_gemm_bf16_kernel<gate_up>");
     }
     const int NB = I / 128;
-    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<true>, dim3(persistent_grid(tiles_bound * NB, 2)),
+    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<true>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                        dim3(kThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
                        (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E,
                        offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale, I);
@@ -654,7 +696,7 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
         return check_launch("ffn_gemm_bf16_kernel<down>");
     }
     const int NB = H / 256;
-    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<false>, dim3(persistent_grid(tiles_bound * NB, 2)),
+    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<false>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                        dim3(kThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
                        w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
                        max_rows, I, H, NB, y_perm, nullptr, H);
