@@ -65,6 +65,9 @@ struct TileMap {
 // bm rows
 __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int n_groups,
                               int max_rows, int bm) {
+    // every thread of the workgroup calls this (it holds barriers); the first
+    // 256 do the work, so any workgroup size >= 256 is fine
+    const bool act = threadIdx.x < 256;
     const int per = (n_groups + 255) / 256;
     const int g0 = threadIdx.x * per;
     int local[5];  // per <= 5 since n_groups <= 1025 (+ slack)
@@ -73,29 +76,31 @@ __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, 
     for (int i = 0; i < 5; ++i) {
         const int g = g0 + i;
         int nt = 0;
-        if (i < per && g < n_groups) {
+        if (act && i < per && g < n_groups) {
             const int m = clamp_row(offsets[g + 1], max_rows) - clamp_row(offsets[g], max_rows);
             nt = m > 0 ? (m + bm - 1) / bm : 0;
         }
         local[i] = nt;
         sum += nt;
     }
-    tm.part[threadIdx.x] = sum;
+    if (act) tm.part[threadIdx.x] = sum;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-        const int v = threadIdx.x >= off ? tm.part[threadIdx.x - off] : 0;
+        const int v = act && threadIdx.x >= off ? tm.part[threadIdx.x - off] : 0;
         __syncthreads();
-        tm.part[threadIdx.x] += v;
+        if (act) tm.part[threadIdx.x] += v;
         __syncthreads();
     }
-    int run = tm.part[threadIdx.x] - sum;
+    if (act) {
+        int run = tm.part[threadIdx.x] - sum;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int g = g0 + i;
-        if (i < per && g < n_groups) tm.start[g] = run;
-        run += local[i];
+        for (int i = 0; i < 5; ++i) {
+            const int g = g0 + i;
+            if (i < per && g < n_groups) tm.start[g] = run;
+            run += local[i];
+        }
+        if (threadIdx.x == 255) tm.start[n_groups] = tm.part[255];
     }
-    if (threadIdx.x == 255) tm.start[n_groups] = tm.part[255];
     __syncthreads();
     return tm.start[n_groups];
 }
@@ -560,6 +565,224 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+// ============================================================================ fp8, LDS ring
+// Tiles of 128 tokens x 256 weight rows, 8 waves. The K step (128) of both
+// operand tiles arrives by direct global->LDS loads (global_load_lds_dwordx4)
+// into a ring of three stages, each its own __shared__ object so the
+// compiler can tell the stage being filled from the one being read and does
+// not drain the ring before every LDS read. In-flight data thus lives in
+// LDS; registers hold 2 x 8 accumulator blocks per wave, and two waves per
+// SIMD overlap one's MFMAs with the other's scaling and waits. An expert with
+// up to 128 rows streams its weights exactly once.
+//   SwiGLU: LDS weight rows q < 128 are gate rows nb*128 + q, q >= 128 the up
+//     rows I + nb*128 + q - 128; wave w owns q = 16w + [0,16) and 128 + the
+//     same (A columns nb*128 + 16w + [0,16)).
+//   Down: q -> w2 row nb*256 + q; wave w owns q = 32w + [0,32).
+// LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row q sits at
+// physical chunk c ^ ((q >> 1) & 7), which makes the 16-row operand reads
+// conflict-free. Every wave issues the same 7 loads per step: 4 weight
+// pieces, 2 activation pieces, 1 scale piece (waves 2..7 re-read the scales
+// of waves 0 and 1 into an unused part), so one vmcnt value is exact for all.
+constexpr int kLTM = 128;    // tokens per tile
+constexpr int kLTN = 256;    // weight rows per tile
+constexpr int kLWaves = 8;
+constexpr int kLThreads = kLWaves * 64;
+
+struct Fp8Stage {
+    uint8_t w[kLTN * kBK];       // 32 KB
+    uint8_t x[kLTM * kBK];       // 16 KB
+    float xs[kLWaves * 64];      // activation scales of the step (rows 0..127 used)
+};
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+__device__ __forceinline__ int swz(int q, int c) { return (c ^ ((q >> 1) & 7)) * 16; }
+
+template <bool kSwiGLU>
+__global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
+    const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
+    int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
+    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
+    __shared__ __attribute__((aligned(1024))) Fp8Stage st0;
+    __shared__ __attribute__((aligned(1024))) Fp8Stage st1;
+    __shared__ __attribute__((aligned(1024))) Fp8Stage st2;
+    __shared__ TileMap tm;
+    __shared__ float wsc[2][64];  // weight block scales of the item: [block][k step]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int nk = K / kBK;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kLTM) * NB;
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = gridDim.x >> 3;
+    const int i_lo = (int)((long)n_items * xcd / 8);
+    const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
+
+    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
+        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kLTM);
+        const int nb = item % NB;
+        const bool routed = tile.group < n_routed;
+        const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
+        const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
+        auto grow = [&](int q) {  // global weight row of LDS row q
+            if (kSwiGLU) return q < 128 ? nb * 128 + q : Nw / 2 + nb * 128 + (q - 128);
+            return nb * 256 + q;
+        };
+        for (int i = threadIdx.x; i < 2 * nk; i += kLThreads) {
+            const int blk = i / nk, kc = i % nk;
+            wsc[blk][kc] = Sg[(size_t)(grow(blk * 128) / kBK) * nk + kc];
+        }
+        // per-lane global sources of this wave's 7 loads (k step 0)
+        const uint8_t* wsrc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = (wave * 4 + i) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((q >> 1) & 7);
+            wsrc[i] = Wg + (size_t)grow(q) * K + c * 16;
+        }
+        const uint8_t* xsrc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (wave * 2 + i) * 8 + (lane >> 3);
+            const int rr = r < tile.rows ? r : tile.rows - 1;
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            xsrc[i] = X + (size_t)(tile.row0 + rr) * K + c * 16;
+        }
+        const int sr = (wave & 1) * 64 + lane;
+        const float* ssrc = Xs + (size_t)(tile.row0 + (sr < tile.rows ? sr : tile.rows - 1)) * nk;
+        const int nms = (tile.rows + 15) >> 4;
+
+        auto issue = [&](int kc, Fp8Stage& S) {
+            kc = kc < nk ? kc : nk - 1;
+            const size_t ko = (size_t)kc * kBK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + ko, &S.w[(wave * 4 + i) * 1024]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + ko, &S.x[(wave * 2 + i) * 1024]);
+            lds_dma4(ssrc + kc, &S.xs[wave * 64]);
+        };
+
+        f32x4 acc[2][8];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        auto compute = [&](int kc, const Fp8Stage& S) {
+            u32x8 a[2];
+            float sw[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int q = kSwiGLU ? s * 128 + 16 * wave + li : 32 * wave + 16 * s + li;
+                const uint8_t* row = &S.w[q * kBK];
+                a[s] = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(row + swz(q, lk)),
+                                               *reinterpret_cast<const u32x4*>(row + swz(q, lk + 4)),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+                sw[s] = wsc[kSwiGLU ? s : (wave >> 2)][kc];
+            }
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                if (ms < nms) {
+                    const int r = ms * 16 + li;
+                    const uint8_t* row = &S.x[r * kBK];
+                    const u32x8 b = __builtin_shufflevector(
+                        *reinterpret_cast<const u32x4*>(row + swz(r, lk)),
+                        *reinterpret_cast<const u32x4*>(row + swz(r, lk + 4)), 0, 1, 2, 3, 4, 5, 6, 7);
+                    const float sx = S.xs[r];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const f32x4 p = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, b));
+                        const float f = sw[s] * sx;
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) acc[s][ms][r4] = __builtin_fmaf(p[r4], f, acc[s][ms][r4]);
+                    }
+                }
+            }
+        };
+
+        // A single top-tested loop with guarded steps: exits from the middle of
+        // the body make the compiler's wait analysis drain the ring (vmcnt 0)
+        // before the first LDS read after the back edge.
+        issue(0, st0);
+        issue(1, st1);
+        for (int j = 0; j < nk; j += 3) {
+            wait_vmcnt<7>();
+            barrier_only();
+            issue(j + 2, st2);
+            compute(j, st0);
+            wait_vmcnt<7>();
+            barrier_only();
+            issue(j + 3, st0);
+            if (j + 1 < nk) compute(j + 1, st1);
+            wait_vmcnt<7>();
+            barrier_only();
+            issue(j + 4, st1);
+            if (j + 2 < nk) compute(j + 2, st2);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();  // the ring and wsc are reused below and by the next item
+
+        // epilogue: lane holds D[n = q0(s) + 4*lk + r4][m = ms*16 + li]
+        if (kSwiGLU) {
+            float* red = reinterpret_cast<float*>(st0.x);  // [8 waves][128 rows], ring is idle
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                float mx = 0.f;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    acc[0][ms][r4] = silu_mul(acc[0][ms][r4], acc[1][ms][r4]);
+                    mx = fmaxf(mx, fabsf(acc[0][ms][r4]));
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                if (lk == 0) red[wave * kLTM + ms * 16 + li] = mx;
+            }
+            __syncthreads();
+            uint8_t* codes = reinterpret_cast<uint8_t*>(out);
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                const int m = ms * 16 + li;
+                if (ms < nms && m < tile.rows) {
+                    float mx = red[m];
+#pragma unroll
+                    for (int v = 1; v < kLWaves; ++v) mx = fmaxf(mx, red[v * kLTM + m]);
+                    const float sc = block_scale(mx);
+                    uint8_t* orow = codes + (size_t)(tile.row0 + m) * ldo;
+                    const int col = nb * 128 + 16 * wave + 4 * lk;
+                    *reinterpret_cast<uint32_t*>(orow + col) = pack_e4m3x4(
+                        clamp_e4m3(acc[0][ms][0] / sc), clamp_e4m3(acc[0][ms][1] / sc),
+                        clamp_e4m3(acc[0][ms][2] / sc), clamp_e4m3(acc[0][ms][3] / sc));
+                    if (wave == 0 && lk == 0) out_scale[(size_t)(tile.row0 + m) * (ldo / kBK) + nb] = sc;
+                }
+            }
+            __syncthreads();
+        } else {
+            uint16_t* y = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                const int m = ms * 16 + li;
+                if (ms < nms && m < tile.rows) {
+                    uint16_t* orow = y + (size_t)(tile.row0 + m) * ldo;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int col = nb * 256 + 32 * wave + 16 * s + 4 * lk;
+                        *reinterpret_cast<uint2*>(orow + col) =
+                            make_uint2(pack_bf16x2(acc[s][ms][0], acc[s][ms][1]),
+                                       pack_bf16x2(acc[s][ms][2], acc[s][ms][3]));
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ============================================================================ fp32
 // Plain VALU kernels for fp32 layers (small shapes): one thread per output.
 __device__ __forceinline__ int group_of(const int32_t* offsets, int n_groups, int r) {
@@ -667,6 +890,15 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
         return check_launch("ffn_gemm_bf16_kernel<gate_up>");
     }
     const int NB = I / 128;
+    if (H / kBK <= 64) {  // LDS-ring kernel: the item's weight scales fit its 64-step table
+        const long tl = (long)(max_rows + kLTM - 1) / kLTM + n_groups;
+        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<true>, dim3(persistent_grid_xcd(tl * NB, 1)),
+                           dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
+                           (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
+                           w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale,
+                           I);
+        return check_launch("ffn_gemm_fp8_lds_kernel<gate_up>");
+    }
     hipLaunchKernelGGL(ffn_gemm_fp8_kernel<true>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                        dim3(kThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
                        (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E,
@@ -696,6 +928,14 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
         return check_launch("ffn_gemm_bf16_kernel<down>");
     }
     const int NB = H / 256;
+    if (I / kBK <= 64) {
+        const long tl = (long)(max_rows + kLTM - 1) / kLTM + n_groups;
+        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<false>, dim3(persistent_grid_xcd(tl * NB, 1)),
+                           dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
+                           w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
+                           max_rows, I, H, NB, y_perm, nullptr, H);
+        return check_launch("ffn_gemm_fp8_lds_kernel<down>");
+    }
     hipLaunchKernelGGL(ffn_gemm_fp8_kernel<false>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                        dim3(kThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
                        w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
