@@ -88,7 +88,8 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, moe
  *   slot_to_row [T*k] (out; -1 = not local),
  *   x_perm [T*k+T, H] (out): x[token(row)] as a bit copy (perm_dt == x_dt)
  *   or, for perm_dt = MOE_FP8_E4M3 with bf16 x, e4m3 codes with
- *   x_perm_scale [T*k+T, H/128] fp32 (out): per 1x128 block s = amax/448 (1 for
+ *   x_perm_scale [H/128, T*k+T] fp32 (out, K-major: block b of row r at
+ *   b*(T*k+T) + r): per 1x128 block s = amax/448 (1 for
  *   an all-zero block), code = e4m3(clamp(v/s, +-448)), fp32 division, round to
  *   nearest even. x and x_perm may both be NULL (maps and counts only).
  * ids outside the local range (including negative ones) are simply not local.
@@ -128,7 +129,8 @@ typedef struct moe_expert_weights {
  * between the GEMMs. fp8: A is quantised per 1x128 block exactly like x_perm
  * (fp32 scale amax/448, round to nearest even), and block scales are applied
  * to each 128-deep partial product.
- *   x_perm [max_rows, H] (+ x_perm_scale [max_rows, H/128] for fp8),
+ *   x_perm [max_rows, H] (+ x_perm_scale [H/128, max_rows] for fp8, K-major
+ *   as moe_permute writes it when max_rows = T*k+T),
  *   expert_offsets [n_groups+1] (device; as written by moe_permute),
  *   y_perm [max_rows, H] (out): bf16 (fp32 for dt = MOE_F32).
  * max_rows bounds offsets[n_groups] (T*k+T for the maps of moe_permute).

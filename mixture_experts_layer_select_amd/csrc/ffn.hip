@@ -105,23 +105,54 @@ __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, 
     return tm.start[n_groups];
 }
 
-__device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __restrict__ offsets,
-                                         int n_groups, int max_rows, int mt, int bm) {
+__device__ __forceinline__ int group_of(const TileMap& tm, int n_groups, int mt) {
     int lo = 0, hi = n_groups - 1;  // last g with start[g] <= mt
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (tm.start[mid] <= mt) lo = mid;
         else hi = mid - 1;
     }
+    return lo;
+}
+
+// The nt = ceil(m / bm) tiles of a group with m rows split it evenly: tile t
+// holds rows [floor(t m / nt), floor((t + 1) m / nt)), between 1 and bm rows.
+// Tiles of one group then carry the same work, so the workgroups that share
+// an n-block's weights through L2 (item_at) stay in step.
+__device__ __forceinline__ MTile make_tile(const TileMap& tm, const int32_t* __restrict__ offsets,
+                                           int max_rows, int g, int mt, int bm) {
     MTile t;
-    const int r0 = clamp_row(offsets[lo], max_rows);
-    const int r1 = clamp_row(offsets[lo + 1], max_rows);
-    const int row0 = r0 + (mt - tm.start[lo]) * bm;
+    const int r0 = clamp_row(offsets[g], max_rows);
+    const int m = clamp_row(offsets[g + 1], max_rows) - r0;
+    const int nt = tm.start[g + 1] - tm.start[g];
+    const int i = mt - tm.start[g];
+    const int a = (int)((long)i * m / nt);
+    const int b = (int)((long)(i + 1) * m / nt);
     // the same for every lane: keep it in scalar registers
-    t.group = __builtin_amdgcn_readfirstlane(lo);
-    t.row0 = __builtin_amdgcn_readfirstlane(row0);
-    t.rows = __builtin_amdgcn_readfirstlane(min(bm, r1 - row0));
+    t.group = __builtin_amdgcn_readfirstlane(g);
+    t.row0 = __builtin_amdgcn_readfirstlane(r0 + a);
+    t.rows = __builtin_amdgcn_readfirstlane(b - a);
     return t;
+}
+
+__device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __restrict__ offsets,
+                                         int n_groups, int max_rows, int mt, int bm) {
+    return make_tile(tm, offsets, max_rows, group_of(tm, n_groups, mt), mt, bm);
+}
+
+// Item -> (M tile, n-block) with the M tiles of one n-block of a group
+// consecutive: workgroups that run side by side on one XCD then read that
+// n-block's weights once from HBM and share them through the XCD's L2. A
+// group owns items [start[g]*NB, start[g+1]*NB) in this order as well.
+__device__ __forceinline__ MTile item_at(const TileMap& tm, const int32_t* __restrict__ offsets,
+                                         int n_groups, int max_rows, int item, int NB, int bm,
+                                         int& nb) {
+    const int g = group_of(tm, n_groups, item / NB);
+    const int t0 = tm.start[g];
+    const int tg = tm.start[g + 1] - t0;
+    const int local = item - t0 * NB;
+    nb = __builtin_amdgcn_readfirstlane(local / tg);
+    return make_tile(tm, offsets, max_rows, g, t0 + local % tg, bm);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -199,8 +230,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
     const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
 
     for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
-        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kTM);
-        const int nb = item % NB;
+        int nb;
+        const MTile tile = item_at(tm, offsets, n_groups, max_rows, item, NB, kTM, nb);
         const uint16_t* Wg = tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
         int ra, rb;
         if (kSwiGLU) {
@@ -412,7 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int xrow = 16 * wave + li;
         const int xrr = xrow < tile.rows ? xrow : tile.rows - 1;
         const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 16 * lk);
-        const float* ssrc = Xs + (size_t)(tile.row0 + xrr) * nk;
+        const float* ssrc = Xs + tile.row0 + xrr;  // K-major: step kc at kc * max_rows
 
         f32x4 acc[4][4];
 #pragma unroll
@@ -439,7 +470,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int ko = kc * (kBK / 16);
             xr[0] = xsrc[ko];
             xr[1] = xsrc[ko + 4];
-            xsr = ssrc[kc];
+            xsr = ssrc[(size_t)kc * max_rows];
         };
         auto store_x = [&](int buf) {
             if (xown) {
@@ -541,7 +572,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                             pack_e4m3x4(clamp_e4m3(a[h][ms][0] / sc), clamp_e4m3(a[h][ms][1] / sc),
                                         clamp_e4m3(a[h][ms][2] / sc), clamp_e4m3(a[h][ms][3] / sc));
                     }
-                    if (wave == 0 && lk == 0) out_scale[(size_t)(tile.row0 + m) * (ldo / kBK) + nb] = sc;
+                    if (wave == 0 && lk == 0) out_scale[(size_t)nb * max_rows + tile.row0 + m] = sc;
                 }
             }
             __syncthreads();  // red[] is reused by the next item
@@ -566,32 +597,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // ============================================================================ fp8, LDS ring
-// Tiles of 128 tokens x 256 weight rows, 8 waves. The K step (128) of both
-// operand tiles arrives by direct global->LDS loads (global_load_lds_dwordx4)
-// into a ring of three stages, each its own __shared__ object so the
-// compiler can tell the stage being filled from the one being read and does
-// not drain the ring before every LDS read. In-flight data thus lives in
-// LDS; registers hold 2 x 8 accumulator blocks per wave, and two waves per
-// SIMD overlap one's MFMAs with the other's scaling and waits. An expert with
-// up to 128 rows streams its weights exactly once.
-//   SwiGLU: LDS weight rows q < 128 are gate rows nb*128 + q, q >= 128 the up
-//     rows I + nb*128 + q - 128; wave w owns q = 16w + [0,16) and 128 + the
-//     same (A columns nb*128 + 16w + [0,16)).
-//   Down: q -> w2 row nb*256 + q; wave w owns q = 32w + [0,32).
-// LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row q sits at
-// physical chunk c ^ ((q >> 1) & 7), which makes the 16-row operand reads
-// conflict-free. Every wave issues the same 7 loads per step: 4 weight
-// pieces, 2 activation pieces, 1 scale piece (waves 2..7 re-read the scales
-// of waves 0 and 1 into an unused part), so one vmcnt value is exact for all.
-constexpr int kLTM = 128;    // tokens per tile
-constexpr int kLTN = 256;    // weight rows per tile
+// Tiles of 256 tokens x 256 weight rows, 8 waves; wave w owns 32 weight rows
+// and all 256 tokens, i.e. 2 x 16 blocks of 16x16 accumulators (128 fp32 per
+// lane). Weight rows are private to a wave, so they stream from global memory
+// straight into a 3-slot register ring (MFMA A operand); the activation tile
+// of each K step (128), shared by all waves, arrives by direct global->LDS
+// loads (global_load_lds_dwordx4) into a 3-stage ring, each stage its own
+// __shared__ object so the compiler can tell the stage being filled from the
+// one being read. Steps j+1 and j+2 are in flight while step j computes.
+// Every wave issues the same 9 loads per step (2 weight fragments x 2 halves,
+// 4 activation pieces, 1 scale piece), so one vmcnt value is exact for all.
+// An expert with up to 256 rows streams each weight byte once; larger ones
+// run their M tiles of one n-block side by side (item_at) and share it
+// through L2.
+//   SwiGLU: the item covers intermediate columns nb*128 + [0,128); wave w
+//     owns gate rows nb*128 + 16w + [0,16) (s = 0) and the up rows I + the
+//     same (s = 1).
+//   Down: wave w owns w2 rows nb*256 + 32w + 16s + [0,16).
+// Lane (li, lk) holds the 32 codes at bytes 16lk + [0,16) and 64 + 16lk +
+// [0,16) of a row's 128-byte step, for weights and activations alike. LDS
+// activation rows are 128 bytes; chunk c of row r sits at physical chunk
+// c ^ ((r >> 1) & 7), which makes the 16-row operand reads conflict-free.
+// Activation scales are K-major ([K/128][max_rows]): one step's scales of a
+// tile are one contiguous run.
+constexpr int kLTM = 256;         // tokens per tile
 constexpr int kLWaves = 8;
 constexpr int kLThreads = kLWaves * 64;
+constexpr int kLMaxSteps = 128;   // K <= 16384
 
-struct Fp8Stage {
-    uint8_t w[kLTN * kBK];       // 32 KB
-    uint8_t x[kLTM * kBK];       // 16 KB
-    float xs[kLWaves * 64];      // activation scales of the step (rows 0..127 used)
+struct XStage {
+    uint8_t x[kLTM * kBK];  // 32 KB
+    float xs[2 * kLTM];     // scales of the step: [0,256) used, the rest takes the
+                            // duplicate scale loads of waves 4..7
 };
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
@@ -600,7 +637,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
 __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
 }
-__device__ __forceinline__ int swz(int q, int c) { return (c ^ ((q >> 1) & 7)) * 16; }
+__device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) * 16; }
 
 template <bool kSwiGLU>
 __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
@@ -608,11 +645,12 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
     int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
     int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
-    __shared__ __attribute__((aligned(1024))) Fp8Stage st0;
-    __shared__ __attribute__((aligned(1024))) Fp8Stage st1;
-    __shared__ __attribute__((aligned(1024))) Fp8Stage st2;
+    __shared__ __attribute__((aligned(1024))) XStage st0;
+    __shared__ __attribute__((aligned(1024))) XStage st1;
+    __shared__ __attribute__((aligned(1024))) XStage st2;
     __shared__ TileMap tm;
-    __shared__ float wsc[2][64];  // weight block scales of the item: [block][k step]
+    __shared__ float wsc[2][kLMaxSteps];  // weight block scales of the item: [block][k step]
+    __shared__ float red[kSwiGLU ? kLWaves * kLTM : 1];  // SwiGLU row amax per wave
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -626,114 +664,159 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
 
     for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
-        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kLTM);
-        const int nb = item % NB;
+        int nb;
+        const MTile tile = item_at(tm, offsets, n_groups, max_rows, item, NB, kLTM, nb);
         const bool routed = tile.group < n_routed;
         const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
         const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
-        auto grow = [&](int q) {  // global weight row of LDS row q
-            if (kSwiGLU) return q < 128 ? nb * 128 + q : Nw / 2 + nb * 128 + (q - 128);
-            return nb * 256 + q;
-        };
+        // the two 128-row weight blocks of the item
+        const int blk0 = kSwiGLU ? nb : 2 * nb;
+        const int blk1 = kSwiGLU ? Nw / 2 / kBK + nb : 2 * nb + 1;
         for (int i = threadIdx.x; i < 2 * nk; i += kLThreads) {
-            const int blk = i / nk, kc = i % nk;
-            wsc[blk][kc] = Sg[(size_t)(grow(blk * 128) / kBK) * nk + kc];
+            const int h = i / nk, kc = i % nk;
+            wsc[h][kc] = Sg[(size_t)(h ? blk1 : blk0) * nk + kc];
         }
-        // per-lane global sources of this wave's 7 loads (k step 0)
-        const uint8_t* wsrc[4];
+        // this wave's weight fragments (A operand): 32-bit lane offsets from the
+        // item's (scalar) weight base, so the loads take the SGPR-base form
+        uint32_t woff[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int row = kSwiGLU ? s * (Nw / 2) + nb * 128 + 16 * wave + li
+                                    : nb * 256 + 32 * wave + 16 * s + li;
+            woff[s] = (uint32_t)row * K + 16 * lk;
+        }
+        const int wblk = kSwiGLU ? 0 : (wave >> 2);  // SwiGLU: s selects the block
+        // activation pieces p = 8i + wave hold LDS rows 8p + [0,8); lane: row
+        // 8p + lane/8 (clamped to the tile), physical chunk lane%8
+        const uint8_t* Xt = X + (size_t)tile.row0 * K;
+        uint32_t xoff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q = (wave * 4 + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((q >> 1) & 7);
-            wsrc[i] = Wg + (size_t)grow(q) * K + c * 16;
-        }
-        const uint8_t* xsrc[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = (wave * 2 + i) * 8 + (lane >> 3);
+            const int r = (i * 8 + wave) * 8 + (lane >> 3);
             const int rr = r < tile.rows ? r : tile.rows - 1;
             const int c = (lane & 7) ^ ((r >> 1) & 7);
-            xsrc[i] = X + (size_t)(tile.row0 + rr) * K + c * 16;
+            xoff[i] = (uint32_t)rr * K + c * 16;
         }
-        const int sr = (wave & 1) * 64 + lane;
-        const float* ssrc = Xs + (size_t)(tile.row0 + (sr < tile.rows ? sr : tile.rows - 1)) * nk;
+        // scales: wave w loads rows 64(w%4) + lane (clamped) into xs[64w + lane]
+        const int sr = 64 * (wave & 3) + lane;
+        const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1);
+        const float* Xst = Xs + tile.row0;
         const int nms = (tile.rows + 15) >> 4;
 
-        auto issue = [&](int kc, Fp8Stage& S) {
+        u32x8 wr[3][2];
+        auto issue = [&](int kc, auto slot_c, XStage& S) {
+            constexpr int sl = decltype(slot_c)::value;
             kc = kc < nk ? kc : nk - 1;
-            const size_t ko = (size_t)kc * kBK;
+            const uint8_t* xk = Xt + (size_t)kc * kBK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + ko, &S.w[(wave * 4 + i) * 1024]);
+            for (int i = 0; i < 4; ++i) lds_dma16(xk + xoff[i], &S.x[(i * 8 + wave) * 1024]);
+            lds_dma4(Xst + (size_t)kc * max_rows + soff, &S.xs[64 * wave]);
+            const uint8_t* wk = Wg + (size_t)kc * kBK;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + ko, &S.x[(wave * 2 + i) * 1024]);
-            lds_dma4(ssrc + kc, &S.xs[wave * 64]);
+            for (int s = 0; s < 2; ++s)
+                wr[sl][s] = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(wk + woff[s]),
+                                                    *reinterpret_cast<const u32x4*>(wk + woff[s] + 64),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
         };
 
-        f32x4 acc[2][8];
+        f32x4 acc[2][16];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ms = 0; ms < 16; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        auto compute = [&](int kc, const Fp8Stage& S) {
-            u32x8 a[2];
+        // row 16ms + li of the activation tile: the swizzle ((16ms + li) >> 1) & 7
+        // does not depend on ms, so the two 16-byte reads are a per-lane offset
+        // plus the immediate ms * 2048
+        const int bo0 = li * kBK + ((lk ^ ((li >> 1) & 7)) << 4);
+        const int bo1 = li * kBK + (((lk + 4) ^ ((li >> 1) & 7)) << 4);
+        auto load_b = [&](const XStage& S, int ms) {
+            const uint8_t* base = &S.x[ms * 16 * kBK];
+            return __builtin_shufflevector(*reinterpret_cast<const u32x4*>(base + bo0),
+                                           *reinterpret_cast<const u32x4*>(base + bo1),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        // token blocks in pairs (a block past the tile's rows computes on the
+        // clamped duplicate rows and is never stored); the scheduling barriers
+        // keep the compiler from hoisting every B fragment above the
+        // 128 accumulators
+        auto compute = [&](int kc, auto slot_c, const XStage& S) {
+            constexpr int sl = decltype(slot_c)::value;
+            // constant first index: the compiler keeps the table apart from the
+            // ring (a computed row makes it wait for every load in flight)
+            const float g0 = wsc[0][kc], g1 = wsc[1][kc];
             float sw[2];
+            sw[0] = kSwiGLU ? g0 : (wblk ? g1 : g0);
+            sw[1] = kSwiGLU ? g1 : sw[0];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int q = kSwiGLU ? s * 128 + 16 * wave + li : 32 * wave + 16 * s + li;
-                const uint8_t* row = &S.w[q * kBK];
-                a[s] = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(row + swz(q, lk)),
-                                               *reinterpret_cast<const u32x4*>(row + swz(q, lk + 4)),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
-                sw[s] = wsc[kSwiGLU ? s : (wave >> 2)][kc];
-            }
-#pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
+            for (int ms = 0; ms < 16; ms += 2) {
                 if (ms < nms) {
-                    const int r = ms * 16 + li;
-                    const uint8_t* row = &S.x[r * kBK];
-                    const u32x8 b = __builtin_shufflevector(
-                        *reinterpret_cast<const u32x4*>(row + swz(r, lk)),
-                        *reinterpret_cast<const u32x4*>(row + swz(r, lk + 4)), 0, 1, 2, 3, 4, 5, 6, 7);
-                    const float sx = S.xs[r];
+                    const u32x8 b0 = load_b(S, ms);
+                    const u32x8 b1 = load_b(S, ms + 1);
+                    const float sx0 = S.xs[ms * 16 + li];
+                    const float sx1 = S.xs[ms * 16 + 16 + li];
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        const f32x4 p = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, b));
-                        const float f = sw[s] * sx;
+                        const f32x4 p0 = mfma_fp8(__builtin_bit_cast(i32x8, wr[sl][s]),
+                                                  __builtin_bit_cast(i32x8, b0));
+                        const f32x4 p1 = mfma_fp8(__builtin_bit_cast(i32x8, wr[sl][s]),
+                                                  __builtin_bit_cast(i32x8, b1));
+                        const float f0 = sw[s] * sx0, f1 = sw[s] * sx1;
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) acc[s][ms][r4] = __builtin_fmaf(p[r4], f, acc[s][ms][r4]);
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            acc[s][ms][r4] = __builtin_fmaf(p0[r4], f0, acc[s][ms][r4]);
+                            acc[s][ms + 1][r4] = __builtin_fmaf(p1[r4], f1, acc[s][ms + 1][r4]);
+                        }
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using S2 = std::integral_constant<int, 2>;
 
         // A single top-tested loop with guarded steps: exits from the middle of
         // the body make the compiler's wait analysis drain the ring (vmcnt 0)
-        // before the first LDS read after the back edge.
-        issue(0, st0);
-        issue(1, st1);
-        for (int j = 0; j < nk; j += 3) {
-            wait_vmcnt<7>();
+        // before the first LDS read after the back edge. The analysis also
+        // loses track of the ring at the loop header and drains it before the
+        // first step of each iteration; six steps per iteration keep that to
+        // one step in six.
+        issue(0, S0{}, st0);
+        issue(1, S1{}, st1);
+        for (int j = 0; j < nk; j += 6) {
+            wait_vmcnt<9>();
             barrier_only();
-            issue(j + 2, st2);
-            compute(j, st0);
-            wait_vmcnt<7>();
+            issue(j + 2, S2{}, st2);
+            compute(j, S0{}, st0);
+            wait_vmcnt<9>();
             barrier_only();
-            issue(j + 3, st0);
-            if (j + 1 < nk) compute(j + 1, st1);
-            wait_vmcnt<7>();
+            issue(j + 3, S0{}, st0);
+            if (j + 1 < nk) compute(j + 1, S1{}, st1);
+            wait_vmcnt<9>();
             barrier_only();
-            issue(j + 4, st1);
-            if (j + 2 < nk) compute(j + 2, st2);
+            issue(j + 4, S1{}, st1);
+            if (j + 2 < nk) compute(j + 2, S2{}, st2);
+            wait_vmcnt<9>();
+            barrier_only();
+            issue(j + 5, S2{}, st2);
+            if (j + 3 < nk) compute(j + 3, S0{}, st0);
+            wait_vmcnt<9>();
+            barrier_only();
+            issue(j + 6, S0{}, st0);
+            if (j + 4 < nk) compute(j + 4, S1{}, st1);
+            wait_vmcnt<9>();
+            barrier_only();
+            issue(j + 7, S1{}, st1);
+            if (j + 5 < nk) compute(j + 5, S2{}, st2);
         }
         wait_vmcnt<0>();
         __syncthreads();  // the ring and wsc are reused below and by the next item
 
-        // epilogue: lane holds D[n = q0(s) + 4*lk + r4][m = ms*16 + li]
+        // epilogue: lane holds D[n = 16-row block s, row 4*lk + r4][m = ms*16 + li]
         if (kSwiGLU) {
-            float* red = reinterpret_cast<float*>(st0.x);  // [8 waves][128 rows], ring is idle
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
+            for (int ms = 0; ms < 16; ++ms) {
                 float mx = 0.f;
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
@@ -747,7 +830,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
             __syncthreads();
             uint8_t* codes = reinterpret_cast<uint8_t*>(out);
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
+            for (int ms = 0; ms < 16; ++ms) {
                 const int m = ms * 16 + li;
                 if (ms < nms && m < tile.rows) {
                     float mx = red[m];
@@ -759,14 +842,14 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
                     *reinterpret_cast<uint32_t*>(orow + col) = pack_e4m3x4(
                         clamp_e4m3(acc[0][ms][0] / sc), clamp_e4m3(acc[0][ms][1] / sc),
                         clamp_e4m3(acc[0][ms][2] / sc), clamp_e4m3(acc[0][ms][3] / sc));
-                    if (wave == 0 && lk == 0) out_scale[(size_t)(tile.row0 + m) * (ldo / kBK) + nb] = sc;
+                    if (wave == 0 && lk == 0) out_scale[(size_t)nb * max_rows + tile.row0 + m] = sc;
                 }
             }
             __syncthreads();
         } else {
             uint16_t* y = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
+            for (int ms = 0; ms < 16; ++ms) {
                 const int m = ms * 16 + li;
                 if (ms < nms && m < tile.rows) {
                     uint16_t* orow = y + (size_t)(tile.row0 + m) * ldo;
@@ -830,7 +913,7 @@ __global__ void ffn_gemm2_f32_kernel(const float* __restrict__ A, const float* _
 
 struct FfnWs {
     void* a;        // intermediate activations A [max_rows][I]
-    float* a_scale; // fp8 only: [max_rows][I/128]
+    float* a_scale; // fp8 only: [I/128][max_rows] (K-major)
     size_t bytes;
 };
 
@@ -890,7 +973,7 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
         return check_launch("ffn_gemm_bf16_kernel<gate_up>");
     }
     const int NB = I / 128;
-    if (H / kBK <= 64) {  // LDS-ring kernel: the item's weight scales fit its 64-step table
+    if (H / kBK <= kLMaxSteps) {  // LDS-ring kernel: the item's weight scales fit its step table
         const long tl = (long)(max_rows + kLTM - 1) / kLTM + n_groups;
         hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<true>, dim3(persistent_grid_xcd(tl * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
@@ -928,7 +1011,7 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
         return check_launch("ffn_gemm_bf16_kernel<down>");
     }
     const int NB = H / 256;
-    if (I / kBK <= 64) {
+    if (I / kBK <= kLMaxSteps) {
         const long tl = (long)(max_rows + kLTM - 1) / kLTM + n_groups;
         hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<false>, dim3(persistent_grid_xcd(tl * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,

@@ -236,10 +236,11 @@ __global__ __launch_bounds__(256) void perm_gather_copy_kernel(
 }
 
 // bf16 rows -> e4m3 codes + one fp32 scale per 128 elements; H % 128 == 0.
-// 16 lanes own one 128-element block, 8 elements each.
+// 16 lanes own one 128-element block, 8 elements each. Scales are K-major:
+// block b of row r at b * cap + r.
 __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ row_to_slot,
-    const int32_t* __restrict__ offsets, int E_local, long S, int k, int H,
+    const int32_t* __restrict__ offsets, int E_local, long S, int k, int H, long cap,
     uint8_t* __restrict__ x_perm, float* __restrict__ x_scale) {
     const long used = offsets[E_local + 1];
     const int nb = H / 128;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
             uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
             uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
             *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
-            if (sub == 0) x_scale[r * nb + b] = sc;
+            if (sub == 0) x_scale[b * cap + r] = sc;
         }
     }
 }
@@ -337,7 +338,7 @@ static moe_status launch_gather(const void* x, moe_dtype x_dt, int H, moe_dtype 
     const int gather_blocks = (int)std::min<long>(cap, (long)cu * 8);
     if (perm_dt == MOE_FP8_E4M3) {
         hipLaunchKernelGGL(perm_gather_fp8_kernel, dim3(gather_blocks), dim3(256), 0, st,
-                           (const uint16_t*)x, row_to_slot, offsets, E_local, S, k, H,
+                           (const uint16_t*)x, row_to_slot, offsets, E_local, S, k, H, cap,
                            (uint8_t*)x_perm, x_perm_scale);
         return check_launch("perm_gather_fp8_kernel");
     }

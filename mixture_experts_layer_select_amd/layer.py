@@ -87,7 +87,7 @@ class MoELayer:
             row_to_slot=torch.empty(cap, **i32),
             slot_to_row=torch.empty(T * k, **i32),
             x_perm=torch.empty((cap, H), dtype=xdt, device=device),
-            x_perm_scale=torch.empty((cap, H // 128), **f32) if self.fmt == "fp8" else None,
+            x_perm_scale=torch.empty((H // 128, cap), **f32) if self.fmt == "fp8" else None,
             y_perm=torch.empty((cap, H), dtype=act, device=device),
             out=torch.empty((T, H), dtype=act, device=device),
             ws_perm=torch.empty(max(ws_p, 1), dtype=torch.uint8, device=device),

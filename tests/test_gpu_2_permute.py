@@ -37,7 +37,8 @@ def _permute_gpu(ids, x, base, E_local, shared, fp8):
     xp = xs = None
     if x is not None:
         xp = torch.zeros((cap, H), dtype=torch.uint8 if fp8 else x.dtype, device=DEV)
-        xs = torch.zeros((cap, H // 128), dtype=torch.float32, device=DEV) if fp8 else None
+        # scales are K-major: [H/128][cap]
+        xs = torch.zeros((H // 128, cap), dtype=torch.float32, device=DEV) if fp8 else None
     ws_n = L.moe_permute_workspace_size(T, k, E_local)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=DEV)
     xdt = L.BF16 if x is None or x.dtype == torch.bfloat16 else L.F32
@@ -67,7 +68,7 @@ def _check(ids, x, base, E_local, shared, fp8=False, sample_rows=None):
     got = oracle.as_np(xp[torch.from_numpy(rows).to(DEV)].cpu())
     assert np.array_equal(got, xp_ref)
     if fp8:
-        gs = xs[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        gs = xs[:, torch.from_numpy(rows).to(DEV)].t().contiguous().cpu().numpy()
         assert np.array_equal(gs.view(np.uint32), xs_ref.view(np.uint32))
     return ref
 

@@ -32,7 +32,7 @@ def _run(fmt, H, I, sizes, shared, seed=0):
     if fmt == "fp8":
         codes, scales = oracle.quantize_1x128(x.float().cpu().numpy())
         xp = torch.from_numpy(codes).to(DEV)
-        xs = torch.from_numpy(scales).to(DEV)
+        xs = torch.from_numpy(np.ascontiguousarray(scales.T)).to(DEV)  # K-major [H/128][max_rows]
     else:
         xp, xs = x, None
     dt = {"f32": L.F32, "bf16": L.BF16, "fp8": L.FP8_E4M3}[fmt]
@@ -50,7 +50,7 @@ def _run(fmt, H, I, sizes, shared, seed=0):
     if shared:
         groups.append(cpu_dict(sh))
     ref = oracle.expert_ffn(groups, xp[:R].cpu() if fmt == "fp8" else x[:R].cpu(),
-                            None if xs is None else xs[:R].cpu(), offsets, H, I)
+                            None if xs is None else xs[:, :R].t().contiguous().cpu(), offsets, H, I)
     got = y[:R].float().cpu().numpy()
     for g in range(len(sizes)):
         a, b = offsets[g], offsets[g + 1]
