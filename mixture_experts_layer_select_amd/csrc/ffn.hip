@@ -62,9 +62,10 @@ struct TileMap {
 };
 
 // all threads of the block must call; returns the total number of tiles of
-// bm rows
+// bm rows. Only groups whose row count m satisfies lo < m <= hi get tiles
+// (the others get none), so two kernels can split the groups between them.
 __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, int n_groups,
-                              int max_rows, int bm) {
+                              int max_rows, int bm, int lo = 0, int hi = 0x7fffffff) {
     // every thread of the workgroup calls this (it holds barriers); the first
     // 256 do the work, so any workgroup size >= 256 is fine
     const bool act = threadIdx.x < 256;
@@ -78,7 +79,7 @@ __device__ int build_tile_map(TileMap& tm, const int32_t* __restrict__ offsets, 
         int nt = 0;
         if (act && i < per && g < n_groups) {
             const int m = clamp_row(offsets[g + 1], max_rows) - clamp_row(offsets[g], max_rows);
-            nt = m > 0 ? (m + bm - 1) / bm : 0;
+            nt = m > lo && m <= hi ? (m + bm - 1) / bm : 0;
         }
         local[i] = nt;
         sum += nt;
@@ -657,7 +658,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int nk = K / kBK;
-    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kLTM) * NB;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kLTM, 0, kLTM) * NB;
     const int xcd = blockIdx.x & 7;
     const int per_xcd = gridDim.x >> 3;
     const int i_lo = (int)((long)n_items * xcd / 8);
@@ -866,6 +867,220 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     }
 }
 
+// ============================================================================ fp8, large groups
+// Groups of more than 256 rows are compute-bound: tiles of 256 tokens x 256
+// weight rows with both operand tiles of each K step arriving by direct
+// global->LDS loads into one of two stages (distinct __shared__ objects);
+// the next step's loads overlap the current step's MFMAs. 8 waves in a 2 x 4
+// grid: wave (wm, wn) owns tokens wm*128 + [0,128) and 64 weight rows,
+// 8 x 4 blocks of 16x16 accumulators, so each weight row is read from LDS by
+// 2 waves and each activation row by 4 (fewer LDS bytes per MFMA than one
+// wave per 32 weight rows). Every wait drains the wave's loads (vmcnt 0), so
+// the number of loads may differ between waves: activation pieces beyond the
+// tile's rows are skipped.
+//   SwiGLU: LDS weight rows q < 128 are gate rows nb*128 + q, q >= 128 the up
+//     rows I + nb*128 + q - 128; wave wn owns gate q = 32wn + [0,32) (s = 0, 1)
+//     and the up rows 128 + the same (s = 2, 3).
+//   Down: q -> w2 row nb*256 + q; wave wn owns q = 64wn + 16s + [0,16).
+// LDS rows are 128 bytes; chunk c of row q sits at physical chunk
+// c ^ ((q >> 1) & 7).
+constexpr int kGTM = 256;  // tokens per tile
+constexpr int kGTN = 256;  // weight rows per tile
+
+struct BigStage {
+    uint8_t w[kGTN * kBK];  // 32 KB
+    uint8_t x[kGTM * kBK];  // 32 KB
+    float xs[kGTM];         // activation scales of the step
+};
+
+template <bool kSwiGLU>
+__global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
+    const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
+    int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
+    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
+    __shared__ __attribute__((aligned(1024))) BigStage st0;
+    __shared__ __attribute__((aligned(1024))) BigStage st1;
+    __shared__ TileMap tm;
+    __shared__ float wsc[2][kLMaxSteps];  // weight block scales of the item: [block][k step]
+    __shared__ float red[kSwiGLU ? 4 * kGTM : 1];  // SwiGLU row amax per weight quarter
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;
+    const int lk = lane >> 4;
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    const int nk = K / kBK;
+    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kGTM, kLTM) * NB;
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd = gridDim.x >> 3;
+    const int i_lo = (int)((long)n_items * xcd / 8);
+    const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
+
+    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
+        int nb;
+        const MTile tile = item_at(tm, offsets, n_groups, max_rows, item, NB, kGTM, nb);
+        const bool routed = tile.group < n_routed;
+        const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
+        const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
+        const int blk0 = kSwiGLU ? nb : 2 * nb;
+        const int blk1 = kSwiGLU ? Nw / 2 / kBK + nb : 2 * nb + 1;
+        for (int i = threadIdx.x; i < 2 * nk; i += kLThreads) {
+            const int h = i / nk, kc = i % nk;
+            wsc[h][kc] = Sg[(size_t)(h ? blk1 : blk0) * nk + kc];
+        }
+        // piece p = 8i + wave holds LDS rows 8p + [0,8) of both operands; lane:
+        // row 8p + lane/8, physical chunk lane%8
+        const uint8_t* Xt = X + (size_t)tile.row0 * K;
+        uint32_t woff[4], xoff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = (i * 8 + wave) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((q >> 1) & 7);
+            const int row = kSwiGLU ? (q < 128 ? nb * 128 + q : Nw / 2 + nb * 128 + (q - 128))
+                                    : nb * 256 + q;
+            woff[i] = (uint32_t)row * K + c * 16;
+            const int rr = q < tile.rows ? q : tile.rows - 1;
+            xoff[i] = (uint32_t)rr * K + c * 16;
+        }
+        // scales: waves 0..3 load rows 64w + lane (clamped to the tile)
+        const int sr = 64 * wave + lane;
+        const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1);
+        const float* Xst = Xs + tile.row0;
+        const bool s_on = wave < 4 && 64 * wave < tile.rows;
+        const int nms = max(0, min(8, (tile.rows - wm * 128 + 15) >> 4));
+
+        auto issue = [&](int kc, BigStage& S) {
+            const uint8_t* wk = Wg + (size_t)kc * kBK;
+            const uint8_t* xk = Xt + (size_t)kc * kBK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_dma16(wk + woff[i], &S.w[(i * 8 + wave) * 1024]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (64 * i + 8 * wave < tile.rows) lds_dma16(xk + xoff[i], &S.x[(i * 8 + wave) * 1024]);
+            if (s_on) lds_dma4(Xst + (size_t)kc * max_rows + soff, &S.xs[64 * wave]);
+        };
+
+        f32x4 acc[4][8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // activation row wm*128 + 16ms + li: its swizzle depends on li only
+        const int bo0 = (wm * 128 + li) * kBK + ((lk ^ ((li >> 1) & 7)) << 4);
+        const int bo1 = (wm * 128 + li) * kBK + (((lk + 4) ^ ((li >> 1) & 7)) << 4);
+        auto compute = [&](int kc, const BigStage& S) {
+            if (nms == 0) return;
+            u32x8 a[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int q = kSwiGLU ? (s >> 1) * 128 + 32 * wn + 16 * (s & 1) + li : 64 * wn + 16 * s + li;
+                const uint8_t* row = &S.w[q * kBK];
+                a[s] = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(row + swz(q, lk)),
+                                               *reinterpret_cast<const u32x4*>(row + swz(q, lk + 4)),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            // constant first index: the compiler keeps the table apart from the ring
+            const float g0 = wsc[0][kc], g1 = wsc[1][kc];
+            float sw[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) sw[s] = kSwiGLU ? ((s >> 1) ? g1 : g0) : ((wn >> 1) ? g1 : g0);
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                if (ms < nms) {
+                    const uint8_t* base = &S.x[ms * 16 * kBK];
+                    const u32x8 b = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(base + bo0),
+                                                            *reinterpret_cast<const u32x4*>(base + bo1),
+                                                            0, 1, 2, 3, 4, 5, 6, 7);
+                    const float sx = S.xs[wm * 128 + ms * 16 + li];
+                    f32x4 p[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        p[s] = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, b));
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const float f = sw[s] * sx;
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) acc[s][ms][r4] = __builtin_fmaf(p[s][r4], f, acc[s][ms][r4]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        issue(0, st0);
+        for (int j = 0; j < nk; j += 2) {
+            wait_vmcnt<0>();
+            barrier_only();
+            if (j + 1 < nk) issue(j + 1, st1);
+            compute(j, st0);
+            wait_vmcnt<0>();
+            barrier_only();
+            if (j + 2 < nk) issue(j + 2, st0);
+            if (j + 1 < nk) compute(j + 1, st1);
+        }
+        __syncthreads();  // the stages and wsc are reused by the next item
+
+        // epilogue: lane holds D[n = q0(s) + 4*lk + r4][m = wm*128 + ms*16 + li]
+        if (kSwiGLU) {
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                float mx = 0.f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        acc[h][ms][r4] = silu_mul(acc[h][ms][r4], acc[2 + h][ms][r4]);
+                        mx = fmaxf(mx, fabsf(acc[h][ms][r4]));
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                if (lk == 0) red[wn * kGTM + wm * 128 + ms * 16 + li] = mx;
+            }
+            __syncthreads();
+            uint8_t* codes = reinterpret_cast<uint8_t*>(out);
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                const int m = wm * 128 + ms * 16 + li;
+                if (ms < nms && m < tile.rows) {
+                    float mx = red[m];
+#pragma unroll
+                    for (int v = 1; v < 4; ++v) mx = fmaxf(mx, red[v * kGTM + m]);
+                    const float sc = block_scale(mx);
+                    uint8_t* orow = codes + (size_t)(tile.row0 + m) * ldo;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int col = nb * 128 + 32 * wn + 16 * h + 4 * lk;
+                        *reinterpret_cast<uint32_t*>(orow + col) = pack_e4m3x4(
+                            clamp_e4m3(acc[h][ms][0] / sc), clamp_e4m3(acc[h][ms][1] / sc),
+                            clamp_e4m3(acc[h][ms][2] / sc), clamp_e4m3(acc[h][ms][3] / sc));
+                    }
+                    if (wn == 0 && lk == 0) out_scale[(size_t)nb * max_rows + tile.row0 + m] = sc;
+                }
+            }
+            __syncthreads();
+        } else {
+            uint16_t* y = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                const int m = wm * 128 + ms * 16 + li;
+                if (ms < nms && m < tile.rows) {
+                    uint16_t* orow = y + (size_t)(tile.row0 + m) * ldo;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int col = nb * 256 + 64 * wn + 16 * s + 4 * lk;
+                        *reinterpret_cast<uint2*>(orow + col) =
+                            make_uint2(pack_bf16x2(acc[s][ms][0], acc[s][ms][1]),
+                                       pack_bf16x2(acc[s][ms][2], acc[s][ms][3]));
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ============================================================================ fp32
 // Plain VALU kernels for fp32 layers (small shapes): one thread per output.
 __device__ __forceinline__ int group_of(const int32_t* offsets, int n_groups, int r) {
@@ -973,14 +1188,22 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
         return check_launch("ffn_gemm_bf16_kernel<gate_up>");
     }
     const int NB = I / 128;
-    if (H / kBK <= kLMaxSteps) {  // LDS-ring kernel: the item's weight scales fit its step table
-        const long tl = (long)(max_rows + kLTM - 1) / kLTM + n_groups;
-        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<true>, dim3(persistent_grid_xcd(tl * NB, 1)),
+    if (H / kBK <= kLMaxSteps) {  // LDS-ring kernels: the item's weight scales fit the step table
+        // groups of at most 256 rows (one tile each), then the larger ones
+        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<true>, dim3(persistent_grid_xcd((long)n_groups * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
                            (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
                            w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale,
                            I);
-        return check_launch("ffn_gemm_fp8_lds_kernel<gate_up>");
+        moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<gate_up>");
+        if (r) return r;
+        const long tl = 2L * max_rows / kGTM + 1;  // tiles of groups above 256 rows
+        hipLaunchKernelGGL(ffn_gemm_fp8_big_kernel<true>, dim3(persistent_grid_xcd(tl * NB, 1)),
+                           dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
+                           (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
+                           w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale,
+                           I);
+        return check_launch("ffn_gemm_fp8_big_kernel<gate_up>");
     }
     hipLaunchKernelGGL(ffn_gemm_fp8_kernel<true>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                        dim3(kThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
@@ -1012,12 +1235,18 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
     }
     const int NB = H / 256;
     if (I / kBK <= kLMaxSteps) {
-        const long tl = (long)(max_rows + kLTM - 1) / kLTM + n_groups;
-        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<false>, dim3(persistent_grid_xcd(tl * NB, 1)),
+        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<false>, dim3(persistent_grid_xcd((long)n_groups * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
                            w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
                            max_rows, I, H, NB, y_perm, nullptr, H);
-        return check_launch("ffn_gemm_fp8_lds_kernel<down>");
+        moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<down>");
+        if (r) return r;
+        const long tl = 2L * max_rows / kGTM + 1;
+        hipLaunchKernelGGL(ffn_gemm_fp8_big_kernel<false>, dim3(persistent_grid_xcd(tl * NB, 1)),
+                           dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
+                           w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
+                           max_rows, I, H, NB, y_perm, nullptr, H);
+        return check_launch("ffn_gemm_fp8_big_kernel<down>");
     }
     hipLaunchKernelGGL(ffn_gemm_fp8_kernel<false>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
                        dim3(kThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,

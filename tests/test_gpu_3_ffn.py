@@ -83,3 +83,18 @@ def test_ffn_r1_shape_one_expert_two_tiles(fmt):
     """H=7168, I=2048: one routed expert with 80 rows (a full 64-row tile and a
     16-row tail) plus a 3-row shared group."""
     _run(fmt, 7168, 2048, [80, 3], shared=True, seed=2)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_ffn_groups_across_the_tile_height(fmt):
+    """Groups on both sides of 256 rows (the fp8 path runs groups of at most
+    256 rows and larger ones in separate launches): 257 = one row over, 513 =
+    two full tiles and a one-row tail split into three even tiles, 700, and a
+    600-row shared group, between empty and tiny groups."""
+    _run(fmt, 512, 256, [0, 257, 3, 513, 256, 700, 1, 0, 600], shared=True, seed=3)
+
+
+def test_ffn_fp8_r1_shape_large_group():
+    """H=7168, I=2048 with one 300-row expert (two tiles of 150) and a 40-row
+    one: the full-size K loops of both fp8 launches."""
+    _run("fp8", 7168, 2048, [300, 40], shared=False, seed=4)
