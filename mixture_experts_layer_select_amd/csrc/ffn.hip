@@ -158,6 +158,18 @@ __device__ __forceinline__ MTile item_at(const TileMap& tm, const int32_t* __res
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Raw buffer access: a 128-bit descriptor in SGPRs (base, size in bytes) plus
+// a 32-bit lane offset and a scalar offset. Loads need no 64-bit VGPR address
+// arithmetic, and accesses at or beyond `bytes` read zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting on gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t clamp_bytes(size_t n) { return n < 0xffffffffu ? (uint32_t)n : 0xffffffffu; }
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -242,22 +254,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
             ra = nb * 128 + 32 * wave + li;
             rb = ra + 16;
         }
-        const u32x4* wa = reinterpret_cast<const u32x4*>(Wg + (size_t)ra * K + 8 * lk);
-        const u32x4* wb = reinterpret_cast<const u32x4*>(Wg + (size_t)rb * K + 8 * lk);
+        // buffer loads: 32-bit lane offsets against a scalar descriptor, so no
+        // 64-bit VGPR address temporaries, which the register allocator would
+        // otherwise carve out of the weight ring (forcing a wait for the ring's
+        // loads before the address is written)
+        const uint32_t wa = ((uint32_t)ra * K + 8 * lk) * 2;
+        const uint32_t wb = ((uint32_t)rb * K + 8 * lk) * 2;
+        const __amdgpu_buffer_rsrc_t wr_d = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K * 2));
         const int nms = (tile.rows + 15) >> 4;
 
         // activation staging: wave w owns tile rows 16(w + 4q) + [0, 16), q < kOwn;
         // lane (li, lk) copies 64 B of each such row (k = 32c + 8lk pieces)
-        bool xown[kOwn];
         int xrow[kOwn];
-        const u32x4* xsrc[kOwn];
+        uint32_t xoff[kOwn];
+        const __amdgpu_buffer_rsrc_t xr_d =
+            buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K * 2));
 #pragma unroll
         for (int q = 0; q < kOwn; ++q) {
-            const int base = 16 * (wave + 4 * q);
-            xown[q] = base < tile.rows;
-            xrow[q] = base + li;
+            xrow[q] = 16 * (wave + 4 * q) + li;
             const int xrr = xrow[q] < tile.rows ? xrow[q] : tile.rows - 1;
-            xsrc[q] = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 8 * lk);
+            xoff[q] = ((uint32_t)xrr * K + 8 * lk) * 2;
         }
 
         f32x4 acc_a[kSub], acc_b[kSub];
@@ -272,30 +288,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
         auto load_w = [&](int kc, auto slot_c) {
             constexpr int st = decltype(slot_c)::value;
             kc = kc < nk ? kc : nk - 1;
-            const int ko = kc * (kBK / 8);
+            const uint32_t ko = (uint32_t)kc * kBK * 2;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                ring[st][0][c] = wa[ko + 4 * c];
-                ring[st][1][c] = wb[ko + 4 * c];
+                ring[st][0][c] = buffer_load16(wr_d, wa + 64 * c, ko);
+                ring[st][1][c] = buffer_load16(wr_d, wb + 64 * c, ko);
             }
         };
         auto load_x = [&](int kc) {
             kc = kc < nk ? kc : nk - 1;
-            const int ko = kc * (kBK / 8);
+            const uint32_t ko = (uint32_t)kc * kBK * 2;
 #pragma unroll
             for (int q = 0; q < kOwn; ++q)
+                if (16 * (wave + 4 * q) < tile.rows) {  // rows of this wave inside the tile
 #pragma unroll
-                for (int c = 0; c < 4; ++c) xr[q][c] = xsrc[q][ko + 4 * c];
+                    for (int c = 0; c < 4; ++c) xr[q][c] = buffer_load16(xr_d, xoff[q] + 64 * c, ko);
+                }
         };
+        // unconditional: a wave whose rows lie past the tile stores whatever its
+        // registers hold, which no MFMA result that is kept depends on. A
+        // guarded store lets the compiler sink the loads into the guarded
+        // block, behind the weight loads, and then wait for all of them there.
         auto store_x = [&](int buf) {
 #pragma unroll
             for (int q = 0; q < kOwn; ++q) {
-                if (xown[q]) {
-                    uint8_t* d = &xs[buf][xrow[q] * kLdsRowBf16];
+                uint8_t* d = &xs[buf][xrow[q] * kLdsRowBf16];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        *reinterpret_cast<u32x4*>(d + 64 * c + 16 * lk) = xr[q][c];
-                }
+                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(d + 64 * c + 16 * lk) = xr[q][c];
             }
         };
         auto compute = [&](int buf, auto slot_c) {
