@@ -2,8 +2,10 @@
 // dispatch/combine -- this is the GPU-local half) and the row gather used to
 // apply a new expert order ([Moreh-EP] Inter-GPU load balancing).
 //
-// Combine is a memory-bound gather: a workgroup per token (grid-stride),
-// 8 bf16 (16 bytes) per thread per row read, fp32 accumulation in slot order
+// Combine is a memory-bound gather. The unit of work is (token, 1024-column
+// chunk) so a small batch still spreads over every CU (T = 256, H = 7168:
+// 1792 units); a workgroup of 128 threads takes units grid-stride, 8 bf16
+// (16 bytes) per thread per row read, fp32 accumulation in slot order
 // j = 0..k-1 followed by the shared-expert row, then one rounding.
 #include "moe_internal.h"
 
@@ -44,17 +46,23 @@ __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = (uint16_t)f3
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 
 constexpr int kMaxK = 256;
+constexpr int kCombineThreads = 128;
+constexpr int kChunkH = kCombineThreads * 8;  // columns per unit
 
 template <typename TY, typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
-                                                     const int32_t* __restrict__ slot_to_row,
-                                                     const float* __restrict__ topk_w, int T, int k,
-                                                     int H, const int32_t* __restrict__ offsets,
-                                                     int shared_group, TO* __restrict__ out) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const TY* __restrict__ y, const int32_t* __restrict__ slot_to_row,
+    const float* __restrict__ topk_w, int T, int k, int H, const int32_t* __restrict__ offsets,
+    int shared_group, TO* __restrict__ out) {
     __shared__ int rows[kMaxK + 1];
     __shared__ float wts[kMaxK];
     const bool vec = (H & 7) == 0;
-    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    const int nch = (H + kChunkH - 1) / kChunkH;
+    const long n_units = (long)T * nch;
+    for (long u = blockIdx.x; u < n_units; u += gridDim.x) {
+        const int t = (int)(u / nch);
+        const int h_lo = (int)(u % nch) * kChunkH;
+        const int h_hi = min(H, h_lo + kChunkH);
         __syncthreads();
         for (int j = threadIdx.x; j < k; j += blockDim.x) {
             rows[j] = slot_to_row[(size_t)t * k + j];
@@ -63,7 +71,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
         if (threadIdx.x == 0) rows[k] = shared_group >= 0 ? offsets[shared_group] + t : -1;
         __syncthreads();
         if (vec) {
-            for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
+            for (int h = h_lo + threadIdx.x * 8; h < h_hi; h += blockDim.x * 8) {
                 float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 // picks in slot order, 8 at a time: all 8 row loads are issued
                 // before the first multiply-add so their latencies overlap
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y,
                 store8(out + (size_t)t * H + h, acc);
             }
         } else {
-            for (int h = threadIdx.x; h < H; h += blockDim.x) {
+            for (int h = h_lo + threadIdx.x; h < h_hi; h += blockDim.x) {
                 float acc = 0.f;
                 for (int j = 0; j < k; ++j) {
                     const int r = rows[j];
@@ -129,21 +137,22 @@ __global__ void gather_rows_kernel(const uint32_t* __restrict__ src, uint32_t* _
 moe_status launch_combine(const void* y_perm, moe_dtype y_dt, const int32_t* slot_to_row,
                           const float* topk_w, int T, int k, int H, const int32_t* offsets,
                           int shared_group, void* out, moe_dtype out_dt, hipStream_t st) {
-    const int blocks = std::min(T, device_info().cu_count * 8);
+    const long units = (long)T * ((H + kChunkH - 1) / kChunkH);
+    const int blocks = (int)std::max(1L, std::min(units, (long)device_info().cu_count * 16));
     if (y_dt == MOE_BF16 && out_dt == MOE_BF16)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), dim3(blocks), dim3(256), 0, st,
+        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), dim3(blocks), dim3(kCombineThreads), 0, st,
                            (const uint16_t*)y_perm, slot_to_row, topk_w, T, k, H, offsets,
                            shared_group, (uint16_t*)out);
     else if (y_dt == MOE_BF16)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, float>), dim3(blocks), dim3(256), 0, st,
+        hipLaunchKernelGGL((combine_kernel<uint16_t, float>), dim3(blocks), dim3(kCombineThreads), 0, st,
                            (const uint16_t*)y_perm, slot_to_row, topk_w, T, k, H, offsets,
                            shared_group, (float*)out);
     else if (out_dt == MOE_BF16)
-        hipLaunchKernelGGL((combine_kernel<float, uint16_t>), dim3(blocks), dim3(256), 0, st,
+        hipLaunchKernelGGL((combine_kernel<float, uint16_t>), dim3(blocks), dim3(kCombineThreads), 0, st,
                            (const float*)y_perm, slot_to_row, topk_w, T, k, H, offsets,
                            shared_group, (uint16_t*)out);
     else
-        hipLaunchKernelGGL((combine_kernel<float, float>), dim3(blocks), dim3(256), 0, st,
+        hipLaunchKernelGGL((combine_kernel<float, float>), dim3(blocks), dim3(kCombineThreads), 0, st,
                            (const float*)y_perm, slot_to_row, topk_w, T, k, H, offsets,
                            shared_group, (float*)out);
     return check_launch("combine_kernel");
