@@ -969,18 +969,19 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         }
         // piece p = 8i + wave holds LDS rows 8p + [0,8) of both operands; lane:
         // row 8p + lane/8, physical chunk lane%8
+        // piece i covers LDS rows q0 + 64i with q0 = 8*wave + lane/8; the
+        // swizzled chunk c depends on q0 only. Piece i's weight row is piece
+        // 0's plus a uniform distance (64 rows, or the gate->up distance for
+        // SwiGLU's upper half), and its activation row is recomputed at issue
+        // time, so one lane offset of each kind stays live through the loop
+        const int q0 = wave * 8 + (lane >> 3);
+        const int c16 = ((lane & 7) ^ ((q0 >> 1) & 7)) * 16;
         const uint8_t* Xt = X + (size_t)tile.row0 * K;
-        uint32_t woff[4], xoff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = (i * 8 + wave) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((q >> 1) & 7);
-            const int row = kSwiGLU ? (q < 128 ? nb * 128 + q : Nw / 2 + nb * 128 + (q - 128))
-                                    : nb * 256 + q;
-            woff[i] = (uint32_t)row * K + c * 16;
-            const int rr = q < tile.rows ? q : tile.rows - 1;
-            xoff[i] = (uint32_t)rr * K + c * 16;
-        }
+        const uint32_t woff0 = (uint32_t)(kSwiGLU ? nb * 128 + q0 : nb * 256 + q0) * K + c16;
+        auto wdist = [&](int i) -> uint32_t {  // uniform: piece i's weight row - piece 0's
+            if (kSwiGLU) return (uint32_t)(i < 2 ? 64 * i : Nw / 2 + 64 * (i - 2)) * K;
+            return (uint32_t)(64 * i) * K;
+        };
         // scales: waves 0..3 load rows 64w + lane (clamped to the tile)
         const int sr = 64 * wave + lane;
         const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1);
@@ -992,10 +993,14 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
             const uint8_t* wk = Wg + (size_t)kc * kBK;
             const uint8_t* xk = Xt + (size_t)kc * kBK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(wk + woff[i], &S.w[(i * 8 + wave) * 1024]);
+            for (int i = 0; i < 4; ++i) lds_dma16(wk + wdist(i) + woff0, &S.w[(i * 8 + wave) * 1024]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (64 * i + 8 * wave < tile.rows) lds_dma16(xk + xoff[i], &S.x[(i * 8 + wave) * 1024]);
+                if (64 * i + 8 * wave < tile.rows) {
+                    const int r = q0 + 64 * i;
+                    const uint32_t xo = (uint32_t)(r < tile.rows ? r : tile.rows - 1) * K + c16;
+                    lds_dma16(xk + xo, &S.x[(i * 8 + wave) * 1024]);
+                }
             if (s_on) lds_dma4(Xst + (size_t)kc * max_rows + soff, &S.xs[64 * wave]);
         };
 

@@ -98,3 +98,26 @@ def test_ffn_fp8_r1_shape_large_group():
     """H=7168, I=2048 with one 300-row expert (two tiles of 150) and a 40-row
     one: the full-size K loops of both fp8 launches."""
     _run("fp8", 7168, 2048, [300, 40], shared=False, seed=4)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_ffn_every_group_empty(fmt):
+    """No group has a row: the launches find no work and write nothing."""
+    import mixture_experts_layer_select_amd as L
+    H, I, E_local, max_rows = 512, 256, 6, 9
+    cfg = mi.scaled({"bf16": mi.CONFIGS[2], "fp8": mi.CONFIGS[4]}[fmt], H=H, I=I, cid=150)
+    st = mi.stacked_expert_weights(cfg, range(E_local), device=DEV)
+    dt = {"bf16": L.BF16, "fp8": L.FP8_E4M3}[fmt]
+    w = L.make_weights(dt, E_local, H, I, st["w13"], st["w2"], st["w13_scale"], st["w2_scale"])
+    if fmt == "fp8":
+        xp = torch.zeros((max_rows, H), dtype=torch.uint8, device=DEV)
+        xs = torch.ones((H // 128, max_rows), dtype=torch.float32, device=DEV)
+    else:
+        xp, xs = torch.zeros((max_rows, H), dtype=torch.bfloat16, device=DEV), None
+    ws_n = L.moe_expert_ffn_workspace_size(w, max_rows)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=DEV)
+    y = torch.full((max_rows, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    off = torch.zeros(E_local + 1, dtype=torch.int32, device=DEV)
+    L.moe_expert_ffn(w, xp, xs, off, E_local, max_rows, y, ws, ws_n)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
