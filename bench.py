@@ -191,6 +191,15 @@ def profiled_traffic(kernel_key: str, workload: str):
     return None
 
 
+def step_traffic(fmt_key: str, workload: str):
+    """HBM bytes of the timed gate/up step: the bf16 kernel, or the sum of the
+    two fp8 launches (groups of at most 256 rows, then the larger ones)."""
+    if fmt_key != "fp8":
+        return profiled_traffic("gemm_bf16_kernel<true", workload)
+    parts = [profiled_traffic(k, workload) for k in ("gemm_fp8_lds_kernel<true", "gemm_fp8_big_kernel<true")]
+    return None if any(p is None for p in parts) else sum(parts)
+
+
 def cpu_groups(st, sh, ids, base, E_local):
     """Host copies of the experts that the sampled tokens pick (+ shared)."""
     used = sorted({int(e) - base for e in ids.ravel() if 0 <= int(e) - base < E_local})
@@ -327,7 +336,7 @@ def main():
         "roofline": {"kernel": kname, "bound": "mfma" if mfma_bound else "hbm",
                      "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
-                     "traffic": profiled_traffic(f"gemm_{fmt_key}_kernel<true", f"c{cfg.cid}"),
+                     "traffic": step_traffic(fmt_key, f"c{cfg.cid}"),
                      "bytes_per_launch": int(gbytes), "flops_per_launch": gflops,
                      "avg_launch_ms": round(k_ms, 4)},
         "layer_roofline": {"bytes": int(lbytes), "flops": lflops,
