@@ -818,35 +818,90 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
         // the body make the compiler's wait analysis drain the ring (vmcnt 0)
         // before the first LDS read after the back edge. The analysis also
         // loses track of the ring at the loop header and drains it before the
-        // first step of each iteration; six steps per iteration keep that to
-        // one step in six.
+        // first step of each iteration. Gate/up (56 K steps at R1 size) runs
+        // twelve steps per iteration, down (16) six: a longer body makes the
+        // drains rarer, but its last iteration issues (clamped, unused) loads
+        // for every step past the end.
         issue(0, S0{}, st0);
         issue(1, S1{}, st1);
-        for (int j = 0; j < nk; j += 6) {
-            wait_vmcnt<9>();
-            barrier_only();
-            issue(j + 2, S2{}, st2);
-            compute(j, S0{}, st0);
-            wait_vmcnt<9>();
-            barrier_only();
-            issue(j + 3, S0{}, st0);
-            if (j + 1 < nk) compute(j + 1, S1{}, st1);
-            wait_vmcnt<9>();
-            barrier_only();
-            issue(j + 4, S1{}, st1);
-            if (j + 2 < nk) compute(j + 2, S2{}, st2);
-            wait_vmcnt<9>();
-            barrier_only();
-            issue(j + 5, S2{}, st2);
-            if (j + 3 < nk) compute(j + 3, S0{}, st0);
-            wait_vmcnt<9>();
-            barrier_only();
-            issue(j + 6, S0{}, st0);
-            if (j + 4 < nk) compute(j + 4, S1{}, st1);
-            wait_vmcnt<9>();
-            barrier_only();
-            issue(j + 7, S1{}, st1);
-            if (j + 5 < nk) compute(j + 5, S2{}, st2);
+        if constexpr (kSwiGLU) {
+            for (int j = 0; j < nk; j += 12) {
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 2, S2{}, st2);
+                compute(j, S0{}, st0);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 3, S0{}, st0);
+                if (j + 1 < nk) compute(j + 1, S1{}, st1);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 4, S1{}, st1);
+                if (j + 2 < nk) compute(j + 2, S2{}, st2);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 5, S2{}, st2);
+                if (j + 3 < nk) compute(j + 3, S0{}, st0);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 6, S0{}, st0);
+                if (j + 4 < nk) compute(j + 4, S1{}, st1);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 7, S1{}, st1);
+                if (j + 5 < nk) compute(j + 5, S2{}, st2);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 8, S2{}, st2);
+                if (j + 6 < nk) compute(j + 6, S0{}, st0);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 9, S0{}, st0);
+                if (j + 7 < nk) compute(j + 7, S1{}, st1);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 10, S1{}, st1);
+                if (j + 8 < nk) compute(j + 8, S2{}, st2);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 11, S2{}, st2);
+                if (j + 9 < nk) compute(j + 9, S0{}, st0);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 12, S0{}, st0);
+                if (j + 10 < nk) compute(j + 10, S1{}, st1);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 13, S1{}, st1);
+                if (j + 11 < nk) compute(j + 11, S2{}, st2);
+            }
+        } else {
+            for (int j = 0; j < nk; j += 6) {
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 2, S2{}, st2);
+                compute(j, S0{}, st0);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 3, S0{}, st0);
+                if (j + 1 < nk) compute(j + 1, S1{}, st1);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 4, S1{}, st1);
+                if (j + 2 < nk) compute(j + 2, S2{}, st2);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 5, S2{}, st2);
+                if (j + 3 < nk) compute(j + 3, S0{}, st0);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 6, S0{}, st0);
+                if (j + 4 < nk) compute(j + 4, S1{}, st1);
+                wait_vmcnt<9>();
+                barrier_only();
+                issue(j + 7, S1{}, st1);
+                if (j + 5 < nk) compute(j + 5, S2{}, st2);
+            }
         }
         wait_vmcnt<0>();
         __syncthreads();  // the ring and wsc are reused below and by the next item
