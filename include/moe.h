@@ -134,8 +134,9 @@ typedef struct moe_expert_weights {
  *   expert_offsets [n_groups+1] (device; as written by moe_permute),
  *   y_perm [max_rows, H] (out): bf16 (fp32 for dt = MOE_F32).
  * max_rows bounds offsets[n_groups] (T*k+T for the maps of moe_permute).
- * Limits: bf16 needs H % 128 == 0 and I % 128 == 0; fp8 needs H % 256 == 0
- * and I % 128 == 0; E_local <= 1024; n_groups in {E_local, E_local+1} (the
+ * Limits: bf16 needs H % 128 == 0 and I % 128 == 0; fp8 needs H % 256 == 0,
+ * I % 128 == 0 and H, I <= 16384 (the per-item table of weight block
+ * scales); E_local <= 1024; n_groups in {E_local, E_local+1} (the
  * latter needs the shared weights).
  * workspace: moe_expert_ffn_workspace_size(w, max_rows) bytes. */
 size_t moe_expert_ffn_workspace_size(const moe_expert_weights* w, int max_rows);

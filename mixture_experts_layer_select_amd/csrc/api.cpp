@@ -140,6 +140,8 @@ static moe_status check_weights(const moe_expert_weights* w) {
     } else if (w->dt == MOE_FP8_E4M3) {
         REQUIRE(w->H % 256 == 0 && w->I % 128 == 0, MOE_ERR_UNSUPPORTED,
                 "moe_expert_ffn: fp8 needs H %% 256 == 0 and I %% 128 == 0 (H=%d I=%d)", w->H, w->I);
+        REQUIRE(w->H <= 16384 && w->I <= 16384, MOE_ERR_UNSUPPORTED,
+                "moe_expert_ffn: fp8 needs H, I <= 16384 (H=%d I=%d)", w->H, w->I);
         REQUIRE(w->w13_scale && w->w2_scale, MOE_ERR_INVALID_ARG, "moe_expert_ffn: fp8 needs scales");
     } else {
         REQUIRE(w->dt == MOE_F32, MOE_ERR_UNSUPPORTED, "moe_expert_ffn: unknown dt %d", (int)w->dt);

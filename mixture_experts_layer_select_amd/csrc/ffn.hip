@@ -1,29 +1,30 @@
 // Expert FFNs as grouped GEMMs with a device-resident row count per group
-// ([SGLang-H20] SwapAB GEMM: the per-expert M varies from token to token, so
-// tiles must stay small in M; [Moreh-EP] Library optimization: fused MoE
-// kernel, and the shared expert's GEMMs joined into the same launch).
+// ([SGLang-H20] SwapAB GEMM: the per-expert M varies from token to token;
+// [Moreh-EP] Library optimization: fused MoE kernel, the shared expert's GEMMs
+// joined into the same launch, and kernel selection by problem size).
 //
-// Work decomposition. expert_offsets (device) define m-tiles of <= 64 rows
-// per group; a persistent grid walks the (m-tile, n-block) work items; every item streams one panel of expert weight
-// rows over the full K exactly once, so in the memory-bound decode regime
-// each hit expert's weights cross HBM once per 64 rows.
+// Work decomposition. expert_offsets (device) define m-tiles per group; a
+// persistent grid walks the (m-tile, n-block) work items. Every workgroup
+// builds the tile map in LDS from the offsets, so there is no host sync.
 //
-// Inside a work item (4 wavefronts): the 64 x 128 activation tile of each
-// K step is staged in LDS (double buffered) and shared by the 4 waves; each
-// wave streams its own weight rows straight from HBM into registers, one K
-// step ahead of the MFMAs, with 64-byte contiguous pieces per lane. MFMA
-// operands take the weights as A (16 rows of N) and the activations as B
-// (16 rows of M); a group's rows are padded with zeros to the next multiple
-// of 16 and m-subtiles past the group's rows are skipped, so a sparsely hit
-// expert costs one 16-row MFMA side, not a fixed 64.
+// bf16 (ffn_gemm_bf16_kernel): 64-row m-tiles, 4 waves. The activation tile
+//   of each K step (128) is staged in LDS, double buffered, and shared by the
+//   waves; each wave streams its own weight rows from HBM into registers one
+//   step ahead of v_mfma_f32_16x16x32_bf16. Weights are the A operand (16 rows
+//   of N), tokens B (16 rows of M): m-subtiles past a group's rows are
+//   skipped, so a sparsely hit expert costs one 16-row MFMA side.
+// fp8, groups of at most 256 rows (ffn_gemm_fp8_lds_kernel): the whole group
+//   is one tile, so its weights cross HBM once; weights stream into a
+//   register ring per wave, activations through a 3-stage LDS ring filled by
+//   direct global->LDS loads.
+// fp8, larger groups (ffn_gemm_fp8_big_kernel, a second launch): 256 x 256
+//   tiles with both operands through a 2-stage LDS ring, MFMA-bound.
+// fp8 MFMAs are v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales, one
+//   per K step of 128 = one 128x128 weight block and one 1x128 activation
+//   block; the fp32 block scales multiply each partial product.
 //
 // The lane -> K assignment of the loaded pieces is a permutation of the K
 // step; A and B use the same one, so the dot products are unchanged.
-//
-// bf16: v_mfma_f32_16x16x32_bf16, 4 per K step of 128 per (n, m) subtile.
-// fp8:  v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales, one per K
-//       step of 128 = one 128x128 weight block and one 1x128 activation
-//       block; the fp32 block scales multiply each partial product.
 #include "moe_internal.h"
 
 #include <type_traits>
@@ -31,7 +32,6 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 64;      // rows per m-tile (fp8 kernels)
 constexpr int kBigTile = 64;  // rows per m-tile of the bf16 kernels (128 measured slower)
 #ifndef MOE_BF16_OCC
 #define MOE_BF16_OCC 2
@@ -45,12 +45,12 @@ static_assert(kBf16Ring == 2 || kBf16Ring == 3, "bf16 weight ring depth");
 constexpr int kBK = 128;     // K per step
 constexpr int kThreads = 256;
 
-// m-tiles: group g's rows [offsets[g], offsets[g+1]) split into tiles of
-// kBM rows; tiles are numbered group after group. Every workgroup builds the
-// exclusive prefix of tiles per group in LDS once (n_groups <= 1025) and
-// maps a work item to (group, first row, rows) by binary search. Rows at or
-// past max_rows are dropped, so inconsistent offsets cannot push a row index
-// outside the caller's buffers.
+// m-tiles: group g's rows [offsets[g], offsets[g+1]) split into tiles of at
+// most bm rows (the kernel's tile height); tiles are numbered group after
+// group. Every workgroup builds the exclusive prefix of tiles per group in LDS
+// once (n_groups <= 1025) and maps a work item to (group, first row, rows) by
+// binary search. Rows at or past max_rows are dropped, so inconsistent offsets
+// cannot push a row index outside the caller's buffers.
 constexpr int kMaxGroups = 1025;
 
 struct MTile {
@@ -407,227 +407,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
                     *reinterpret_cast<uint2*>(orow + col + 16) =
                         make_uint2(pack_bf16x2(acc_b[ms][0], acc_b[ms][1]),
                                    pack_bf16x2(acc_b[ms][2], acc_b[ms][3]));
-                }
-            }
-        }
-    }
-}
-
-// ============================================================================ fp8
-// SwiGLU (GEMM-1): an item covers 128 intermediate columns = one 1x128 output
-//   quantisation block; wave w owns gate rows n0+32w+16h+li (h = 0, 1) and the
-//   up rows I + the same (n0 = nb*128). Output: A codes [rows][I] + scales
-//   [rows][I/128].
-// Down (GEMM-2): an item covers 256 output columns; wave w owns rows
-//   n0+64w+16s+li, s = 0..3 (n0 = nb*256). Output: y [rows][H] bf16.
-//
-// Same pipeline as the bf16 kernel: the activation codes (and their 1x128
-// scales) of step j+1 are loaded first and staged through LDS, the weight
-// codes of step j+2 go into a 3-deep register ring, and the weight block
-// scales of step j+2 into a small ring of wave-uniform registers. One K step
-// is one 128x128 weight block: MFMA 16x16x128 with unit E8M0 scales gives
-// the block's partial product, which is multiplied by (weight scale x
-// activation scale) and added to the fp32 accumulator. Lane (li, lk) holds
-// the 32 codes at bytes 16lk + [0,16) and 64 + 16lk + [0,16) of its row's
-// 128-byte step, for weights and activations alike.
-constexpr int kLdsRowFp8 = kBK + 16;  // bytes per staged activation row (16 B pad)
-
-template <bool kSwiGLU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_gemm_fp8_kernel(
-    const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
-    const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
-    int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
-    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
-    __shared__ TileMap tm;
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kBM * kLdsRowFp8];
-    __shared__ float xsc[2][kBM];
-    __shared__ float red[4][kBM];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int li = lane & 15;
-    const int lk = lane >> 4;
-    const int nk = K / kBK;   // K steps = scale blocks along K
-    const int n_items = build_tile_map(tm, offsets, n_groups, max_rows, kBM) * NB;
-
-    const int xcd = blockIdx.x & 7;  // XCD-contiguous slices of the items
-    const int per_xcd = gridDim.x >> 3;
-    const int i_lo = (int)((long)n_items * xcd / 8);
-    const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
-
-    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
-        const MTile tile = tile_at(tm, offsets, n_groups, max_rows, item / NB, kBM);
-        const int nb = item % NB;
-        const bool routed = tile.group < n_routed;
-        const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
-        const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
-        int rbase[4];  // first weight row of each 16-row subtile
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (kSwiGLU) rbase[s] = nb * 128 + 32 * wave + 16 * (s & 1) + (s >> 1) * (Nw / 2);
-            else rbase[s] = nb * 256 + 64 * wave + 16 * s;
-        }
-        const u32x4* wp[4];
-        const float* sp[4];  // scale row of each subtile's 128-row block (wave-uniform)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            wp[s] = reinterpret_cast<const u32x4*>(Wg + (size_t)(rbase[s] + li) * K + 16 * lk);
-            sp[s] = Sg + (size_t)(rbase[s] / kBK) * nk;
-        }
-        const int nms = (tile.rows + 15) >> 4;
-
-        // activation staging: wave w owns tile row 16w + li
-        const bool xown = 16 * wave < tile.rows;
-        const int xrow = 16 * wave + li;
-        const int xrr = xrow < tile.rows ? xrow : tile.rows - 1;
-        const u32x4* xsrc = reinterpret_cast<const u32x4*>(X + (size_t)(tile.row0 + xrr) * K + 16 * lk);
-        const float* ssrc = Xs + tile.row0 + xrr;  // K-major: step kc at kc * max_rows
-
-        f32x4 acc[4][4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) acc[s][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
-        u32x8 ring[3][4];
-        float ring_sw[3][4];
-        u32x4 xr[2];
-        float xsr;
-
-        auto load_w = [&](int kc, auto slot_c) {
-            constexpr int st = decltype(slot_c)::value;
-            kc = kc < nk ? kc : nk - 1;
-            const int ko = kc * (kBK / 16);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                ring[st][s] = __builtin_shufflevector(wp[s][ko], wp[s][ko + 4], 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) ring_sw[st][s] = sp[s][kc];
-        };
-        auto load_x = [&](int kc) {
-            kc = kc < nk ? kc : nk - 1;
-            const int ko = kc * (kBK / 16);
-            xr[0] = xsrc[ko];
-            xr[1] = xsrc[ko + 4];
-            xsr = ssrc[(size_t)kc * max_rows];
-        };
-        auto store_x = [&](int buf) {
-            if (xown) {
-                uint8_t* d = &xs[buf][xrow * kLdsRowFp8 + 16 * lk];
-                *reinterpret_cast<u32x4*>(d) = xr[0];
-                *reinterpret_cast<u32x4*>(d + 64) = xr[1];
-                if (lk == 0) xsc[buf][xrow] = xsr;
-            }
-        };
-        auto compute = [&](int buf, auto slot_c) {
-            constexpr int st = decltype(slot_c)::value;
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                if (ms < nms) {
-                    const int m = ms * 16 + li;
-                    const uint8_t* row = &xs[buf][m * kLdsRowFp8 + 16 * lk];
-                    const u32x8 b = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(row),
-                                                            *reinterpret_cast<const u32x4*>(row + 64),
-                                                            0, 1, 2, 3, 4, 5, 6, 7);
-                    const float sx = xsc[buf][m];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const f32x4 p = mfma_fp8(__builtin_bit_cast(i32x8, ring[st][s]),
-                                                 __builtin_bit_cast(i32x8, b));
-                        const float f = ring_sw[st][s] * sx;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[s][ms][r] = __builtin_fmaf(p[r], f, acc[s][ms][r]);
-                    }
-                }
-            }
-        };
-        // activations (2 + 1 loads) first, then weights (8 + 4 scale loads):
-        // waiting until only the 12 weight-side loads remain means the
-        // activations have landed
-        auto step = [&](int j, auto cur, auto nxt) {
-            load_x(j + 1);
-            load_w(j + 2, nxt);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(j & 1, cur);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<12>();
-            store_x((j + 1) & 1);
-            barrier_only();
-        };
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        using S2 = std::integral_constant<int, 2>;
-        load_x(0);
-        load_w(0, S0{});
-        load_w(1, S1{});
-        wait_vmcnt<24>();
-        store_x(0);
-        barrier_only();
-        for (int j = 0;; j += 3) {
-            step(j, S0{}, S2{});
-            if (j + 1 >= nk) break;
-            step(j + 1, S1{}, S0{});
-            if (j + 2 >= nk) break;
-            step(j + 2, S2{}, S1{});
-            if (j + 3 >= nk) break;
-        }
-        wait_vmcnt<0>();
-
-        // epilogue: lane holds D[n = rbase[s] + 4*lk + r][m = ms*16 + li]
-        if (kSwiGLU) {
-            float a[2][4][4];  // [gate subtile][ms][r]
-            float amax[4];
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                float mx = 0.f;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        a[h][ms][r] = silu_mul(acc[h][ms][r], acc[2 + h][ms][r]);
-                        mx = fmaxf(mx, fabsf(a[h][ms][r]));
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                amax[ms] = mx;
-            }
-            if (lk == 0) {
-#pragma unroll
-                for (int ms = 0; ms < 4; ++ms) red[wave][ms * 16 + li] = amax[ms];
-            }
-            __syncthreads();
-            uint8_t* codes = reinterpret_cast<uint8_t*>(out);
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                const int m = ms * 16 + li;
-                if (ms < nms && m < tile.rows) {
-                    const float mx = fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m]));
-                    const float sc = block_scale(mx);
-                    uint8_t* orow = codes + (size_t)(tile.row0 + m) * ldo;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int col = nb * 128 + 32 * wave + 16 * h + 4 * lk;
-                        *reinterpret_cast<uint32_t*>(orow + col) =
-                            pack_e4m3x4(clamp_e4m3(a[h][ms][0] / sc), clamp_e4m3(a[h][ms][1] / sc),
-                                        clamp_e4m3(a[h][ms][2] / sc), clamp_e4m3(a[h][ms][3] / sc));
-                    }
-                    if (wave == 0 && lk == 0) out_scale[(size_t)nb * max_rows + tile.row0 + m] = sc;
-                }
-            }
-            __syncthreads();  // red[] is reused by the next item
-        } else {
-            uint16_t* y = reinterpret_cast<uint16_t*>(out);
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                const int m = ms * 16 + li;
-                if (ms < nms && m < tile.rows) {
-                    uint16_t* orow = y + (size_t)(tile.row0 + m) * ldo;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int col = nb * 256 + 64 * wave + 16 * s + 4 * lk;
-                        *reinterpret_cast<uint2*>(orow + col) =
-                            make_uint2(pack_bf16x2(acc[s][ms][0], acc[s][ms][1]),
-                                       pack_bf16x2(acc[s][ms][2], acc[s][ms][3]));
-                    }
                 }
             }
         }
@@ -1267,7 +1046,6 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                               int max_rows, void* ws, hipStream_t st) {
     FfnWs s = carve(w, max_rows, ws);
     const int H = w->H, I = w->I, E = w->E_local;
-    const long tiles_bound = (long)(max_rows + kBM - 1) / kBM + n_groups;
     if (w->dt == MOE_F32) {
         const int blocks = persistent_grid(((long)max_rows * I + 255) / 256, 8);
         hipLaunchKernelGGL(ffn_gemm1_f32_kernel, dim3(blocks), dim3(256), 0, st, (const float*)x_perm,
@@ -1302,18 +1080,13 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                            I);
         return check_launch("ffn_gemm_fp8_big_kernel<gate_up>");
     }
-    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<true>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
-                       dim3(kThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
-                       (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E,
-                       offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale, I);
-    return check_launch("ffn_gemm_fp8_kernel<gate_up>");
+    return set_error(MOE_ERR_UNSUPPORTED, "fp8 gate/up: H=%d exceeds %d", H, kLMaxSteps * kBK);
 }
 
 moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, int n_groups,
                            int max_rows, void* y_perm, void* ws, hipStream_t st) {
     FfnWs s = carve(w, max_rows, ws);
     const int H = w->H, I = w->I, E = w->E_local;
-    const long tiles_bound = (long)(max_rows + kBM - 1) / kBM + n_groups;
     if (w->dt == MOE_F32) {
         const int blocks = persistent_grid(((long)max_rows * H + 255) / 256, 8);
         hipLaunchKernelGGL(ffn_gemm2_f32_kernel, dim3(blocks), dim3(256), 0, st, (const float*)s.a,
@@ -1345,11 +1118,7 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
                            max_rows, I, H, NB, y_perm, nullptr, H);
         return check_launch("ffn_gemm_fp8_big_kernel<down>");
     }
-    hipLaunchKernelGGL(ffn_gemm_fp8_kernel<false>, dim3(persistent_grid_xcd(tiles_bound * NB, 2)),
-                       dim3(kThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
-                       w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
-                       max_rows, I, H, NB, y_perm, nullptr, H);
-    return check_launch("ffn_gemm_fp8_kernel<down>");
+    return set_error(MOE_ERR_UNSUPPORTED, "fp8 down: I=%d exceeds %d", I, kLMaxSteps * kBK);
 }
 
 }  // namespace moe

@@ -86,6 +86,8 @@ def test_ffn_argument_checks_and_workspace(L):
     _expect(L, L.moe_expert_ffn, "MOE_ERR_WORKSPACE", w, 1, None, 1, 32, 4096 * 9, 1, 1, ws - 1, 0)
     bad = L.make_weights(L.BF16, 32, 7000, 2048, 1, 1)
     _expect(L, L.moe_expert_ffn, "MOE_ERR_UNSUPPORTED", bad, 1, None, 1, 32, 10, 1, 1, 10 ** 9, 0)
+    huge = L.make_weights(L.FP8_E4M3, 32, 16640, 2048, 1, 1, 1, 1)  # H above 16384
+    _expect(L, L.moe_expert_ffn, "MOE_ERR_UNSUPPORTED", huge, 1, 1, 1, 32, 10, 1, 1, 10 ** 9, 0)
     f8 = L.make_weights(L.FP8_E4M3, 32, 7168, 2048, 1, 1)  # no scales
     _expect(L, L.moe_expert_ffn, "MOE_ERR_INVALID_ARG", f8, 1, 1, 1, 32, 10, 1, 1, 10 ** 9, 0)
     assert L.moe_expert_ffn_workspace_size(bad, 10) == 0
