@@ -37,11 +37,6 @@ constexpr int kBigTile = 64;  // rows per m-tile of the bf16 kernels (128 measur
 #define MOE_BF16_OCC 2
 #endif
 constexpr int kBf16Occ = MOE_BF16_OCC;  // waves per SIMD the bf16 GEMMs are compiled for
-#ifndef MOE_BF16_RING
-#define MOE_BF16_RING 2
-#endif
-constexpr int kBf16Ring = MOE_BF16_RING;  // weight register ring depth of the bf16 GEMMs (2 or 3)
-static_assert(kBf16Ring == 2 || kBf16Ring == 3, "bf16 weight ring depth");
 constexpr int kBK = 128;     // K per step
 constexpr int kThreads = 256;
 
@@ -287,7 +282,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
             acc_a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc_b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        u32x4 ring[kBf16Ring][2][4];
+        u32x4 ring[2][2][4];  // weights of steps j (slot j & 1) and j + 1
         u32x4 xr[kOwn][4];
 
         auto load_w = [&](int kc, auto slot_c) {
@@ -337,12 +332,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
                 }
             }
         };
-        // one K step: activations of j+1 first, then weights of j + ring - 1,
-        // compute j, wait for the activations only (the 8 weight loads stay in
-        // flight), stage them, barrier
+        // one K step: activations of j+1 first, then weights of j+1 (a 2-deep
+        // ring measured faster than 3-deep at two workgroups per CU), compute
+        // j, wait for the activations only (the 8 weight loads stay in flight),
+        // stage them, barrier
         auto step = [&](int j, auto cur, auto nxt) {
             load_x(j + 1);
-            load_w(j + kBf16Ring - 1, nxt);
+            load_w(j + 1, nxt);
             __builtin_amdgcn_sched_barrier(0);
             compute(j & 1, cur);
             __builtin_amdgcn_sched_barrier(0);
@@ -350,38 +346,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
             store_x((j + 1) & 1);
             barrier_only();
         };
-        static_assert(kOwn * 4 + 16 < 64, "prologue wait count");
 
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
-        using S2 = std::integral_constant<int, 2>;
-        // prologue: activations of step 0 into LDS, weights of steps 0 .. ring-2
+        // prologue: activations and weights of step 0
         load_x(0);
         load_w(0, S0{});
-        if constexpr (kBf16Ring == 3) {
-            load_w(1, S1{});
-            wait_vmcnt<16>();  // the activations of step 0 (issued first) have landed
-        } else {
-            wait_vmcnt<8>();
-        }
+        wait_vmcnt<8>();  // the activations (issued first) have landed
         store_x(0);
         barrier_only();
-        if constexpr (kBf16Ring == 3) {
-            for (int j = 0;; j += 3) {
-                step(j, S0{}, S2{});
-                if (j + 1 >= nk) break;
-                step(j + 1, S1{}, S0{});
-                if (j + 2 >= nk) break;
-                step(j + 2, S2{}, S1{});
-                if (j + 3 >= nk) break;
-            }
-        } else {
-            for (int j = 0;; j += 2) {
-                step(j, S0{}, S1{});
-                if (j + 1 >= nk) break;
-                step(j + 1, S1{}, S0{});
-                if (j + 2 >= nk) break;
-            }
+        for (int j = 0;; j += 2) {
+            step(j, S0{}, S1{});
+            if (j + 1 >= nk) break;
+            step(j + 1, S1{}, S0{});
+            if (j + 2 >= nk) break;
         }
         wait_vmcnt<0>();  // the clamped tail loads land before registers are reused
 
