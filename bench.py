@@ -44,6 +44,9 @@ def parse():
                     help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="after the eager timed steps, capture one step in a HIP graph and also "
+                         "report the replay time (graph_ms_per_step)")
     return ap.parse_args()
 
 
@@ -306,6 +309,27 @@ def main():
     value = tokens / (ms / 1e3)
     k_ms = float(np.mean([a.elapsed_time(z) for a, z in ev]))
 
+    graph_ms = None
+    if args.graph:
+        # one step captured on a side stream (the eager steps above did every
+        # one-time set-up), then warm-up and timed replays
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step()
+        stream.wait_stream(side)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+        log(f"[bench] graph replay {graph_ms:.4f} ms/step")
+
     counts = b.counts.cpu().numpy()
     n_rows = int(b.offsets[-1].item())
     gbytes, hit = alg_bytes_gate_up(cfg, layer, counts, n_rows)
@@ -346,6 +370,9 @@ def main():
                            "tflops": round(lflops / (ms / 1e3) / 1e12, 2)},
         "cpu_baseline": None,
     }
+    if graph_ms is not None:
+        line["graph_ms_per_step"] = round(graph_ms, 4)
+        line["graph_tokens_per_s"] = round(T / (graph_ms / 1e3), 2)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
