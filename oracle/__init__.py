@@ -50,6 +50,8 @@ def lib() -> C.CDLL:
         L.oracle_expert_ffn.argtypes = [_p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _p]
         L.oracle_combine.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p]
         L.oracle_balanced_partition.argtypes = [_p, _i, _i, _p, _p, _p]
+        L.oracle_coactivation.argtypes = [_p, _i, _i, _i, _p]
+        L.oracle_affinity_partition.argtypes = [_p, _p, _i, _i, _i, _p, _p, _p, _p]
         _lib = L
     return _lib
 
@@ -246,6 +248,30 @@ def balanced_partition(counts, G: int):
     _check(lib().oracle_balanced_partition(_ptr(c), E, G, _ptr(n2o), _ptr(o2n), _ptr(loads)),
            "oracle_balanced_partition")
     return n2o, o2n, loads
+
+
+def coactivation(ids, E: int, hist=None):
+    """Top-k co-activation histogram [E][E] int64, added to ``hist`` when given."""
+    a = _c(ids, np.int32)
+    T, k = a.shape
+    h = np.zeros((E, E), np.int64) if hist is None else _c(hist, np.int64).copy()
+    _check(lib().oracle_coactivation(_ptr(a), T, k, E, _ptr(h)), "oracle_coactivation")
+    return h
+
+
+def affinity_partition(counts, aff, G: int, tol_permille: int):
+    """Balanced partition, then affinity-raising swaps under the load cap."""
+    c = _c(counts, np.int64)
+    A = _c(aff, np.int64)
+    E = c.shape[0]
+    n2o = np.empty(E, np.int32)
+    o2n = np.empty(E, np.int32)
+    loads = np.empty(G, np.int64)
+    intra = np.zeros(1, np.int64)
+    _check(lib().oracle_affinity_partition(_ptr(c), _ptr(A), E, G, tol_permille, _ptr(n2o),
+                                           _ptr(o2n), _ptr(loads), _ptr(intra)),
+           "oracle_affinity_partition")
+    return n2o, o2n, loads, int(intra[0])
 
 
 def to_output(out64, dt: int):

@@ -449,3 +449,96 @@ int oracle_balanced_partition(const int64_t* counts, int E, int G,
     free(L);
     return 0;
 }
+
+/* ------------------------------------------------------- co-activation */
+
+int oracle_coactivation(const int32_t* ids, int T, int k, int E, int64_t* hist) {
+    if (T < 0 || k < 1 || E < 1 || (T > 0 && !ids) || !hist) return -1;
+    for (int t = 0; t < T; ++t) {
+        const int32_t* p = ids + (size_t)t * k;
+        for (int i = 0; i < k; ++i) {
+            int a = p[i];
+            if (a < 0 || a >= E) continue;
+            hist[(size_t)a * E + a] += 1;
+            for (int j = i + 1; j < k; ++j) {
+                int b = p[j];
+                if (b < 0 || b >= E || b == a) continue;
+                hist[(size_t)a * E + b] += 1;
+                hist[(size_t)b * E + a] += 1;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------- affinity partition */
+
+/* sum of aff[e][c] over the members c of group g other than e */
+static int64_t aff_to_group(const int64_t* aff, const int* grp, int E, int e, int g) {
+    int64_t s = 0;
+    for (int c = 0; c < E; ++c)
+        if (c != e && grp[c] == g) s += aff[(size_t)e * E + c];
+    return s;
+}
+
+int oracle_affinity_partition(const int64_t* counts, const int64_t* aff, int E, int G,
+                              int tol_permille, int32_t* new_to_old, int32_t* old_to_new,
+                              int64_t* group_loads, int64_t* intra_affinity) {
+    if (!aff || !intra_affinity || tol_permille < 0) return -1;
+    int rc = oracle_balanced_partition(counts, E, G, new_to_old, old_to_new, group_loads);
+    if (rc) return rc;
+    int S = E / G;
+    int* grp = (int*)malloc(sizeof(int) * (size_t)E);
+    int64_t* L = (int64_t*)malloc(sizeof(int64_t) * (size_t)G);
+    if (!grp || !L) return -2;
+    int64_t Lmax = 0;
+    for (int g = 0; g < G; ++g) {
+        L[g] = group_loads[g];
+        if (L[g] > Lmax) Lmax = L[g];
+        for (int j = 0; j < S; ++j) grp[new_to_old[g * S + j]] = g;
+    }
+    int64_t cap = Lmax * (1000 + tol_permille) / 1000;
+    for (int it = 0; it < 10 * E; ++it) {
+        int64_t best = 0;
+        int ba = -1, bb = -1;
+        for (int a = 0; a < E; ++a) {
+            for (int b = a + 1; b < E; ++b) {
+                int p = grp[a], q = grp[b];
+                if (p == q) continue;
+                int64_t lp = L[p] - counts[a] + counts[b];
+                int64_t lq = L[q] - counts[b] + counts[a];
+                if (lp > cap || lq > cap) continue;
+                /* a moves to q, b moves to p; the pair (a, b) is split before and after */
+                int64_t gain = aff_to_group(aff, grp, E, a, q) - aff[(size_t)a * E + b] +
+                               aff_to_group(aff, grp, E, b, p) - aff[(size_t)b * E + a] -
+                               aff_to_group(aff, grp, E, a, p) - aff_to_group(aff, grp, E, b, q);
+                if (gain > best) {
+                    best = gain;
+                    ba = a;
+                    bb = b;
+                }
+            }
+        }
+        if (ba < 0) break;
+        int p = grp[ba], q = grp[bb];
+        L[p] += counts[bb] - counts[ba];
+        L[q] += counts[ba] - counts[bb];
+        grp[ba] = q;
+        grp[bb] = p;
+    }
+    int64_t total = 0;
+    for (int a = 0; a < E; ++a)
+        for (int b = a + 1; b < E; ++b)
+            if (grp[a] == grp[b]) total += aff[(size_t)a * E + b];
+    *intra_affinity = total;
+    for (int g = 0; g < G; ++g) {
+        int j = 0;
+        for (int e = 0; e < E; ++e)
+            if (grp[e] == g) new_to_old[g * S + j++] = e;
+        group_loads[g] = L[g];
+    }
+    for (int n = 0; n < E; ++n) old_to_new[new_to_old[n]] = n;
+    free(grp);
+    free(L);
+    return 0;
+}

@@ -12,7 +12,7 @@
  *               Library optimization, HIP Graphs.
  *   [SGLang-H20] "Deploying DeepSeek-R1 efficiently on H20-96G together with
  *               SGLang: best practices": Prefill solutions (MoE b_scale),
- *               SwapAB GEMM.
+ *               SwapAB GEMM, Expert Affinity EPLB.
  * The pages fix no precision, reduction order, score function or block
  * format; every such choice below is a stated reading, and the floating point
  * arithmetic of the expert FFN is done in fp64.
@@ -102,6 +102,28 @@ int oracle_combine(const double* y_perm, const int32_t* slot_to_row, const float
  * new_to_old[g*S+j] is the j-th smallest old id of group g. */
 int oracle_balanced_partition(const int64_t* counts, int E, int G,
                               int32_t* new_to_old, int32_t* old_to_new, int64_t* group_loads);
+
+/* Top-k co-activation histogram, accumulated ([SGLang-H20] Expert Affinity
+ * EPLB: track which experts the top-k picks activate together). hist is
+ * [E][E] row-major. For every token, each pick with 0 <= id < E adds 1 to
+ * hist[id][id]; each pair of its picks i < j with valid, distinct ids adds 1
+ * to hist[a][b] and to hist[b][a]. Ids outside [0, E) are ignored. */
+int oracle_coactivation(const int32_t* ids, int T, int k, int E, int64_t* hist);
+
+/* Affinity-aware balanced partition ([Moreh-EP] Inter-GPU load balancing for
+ * the balanced start; [SGLang-H20] Expert Affinity EPLB for the adjustment,
+ * whose steps the page does not give -- this is the reading): start from
+ * oracle_balanced_partition, whose largest group load is L; allow loads up
+ * to cap = floor(L * (1000 + tol_permille) / 1000); then, as long as one
+ * exists, apply the swap of two experts a < b in different groups that keeps
+ * both groups' loads <= cap and raises the total intra-group affinity
+ * sum over groups, sum over pairs a < b in the group, of aff[a][b]
+ * the most (the first such (a, b) in ascending order on ties), at most 10*E
+ * swaps. aff is [E][E] and symmetric. Outputs as the balanced partition plus
+ * *intra_affinity, the final total. */
+int oracle_affinity_partition(const int64_t* counts, const int64_t* aff, int E, int G,
+                              int tol_permille, int32_t* new_to_old, int32_t* old_to_new,
+                              int64_t* group_loads, int64_t* intra_affinity);
 
 #ifdef __cplusplus
 }
