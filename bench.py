@@ -330,6 +330,33 @@ def main():
         graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
         log(f"[bench] graph replay {graph_ms:.4f} ms/step")
 
+    # online rebalancing: what tracking one step costs on the device (the
+    # permute's counts accumulated, the step's picks added to the
+    # co-activation histogram), and the host re-partition from the result
+    ids_all = b.topk_ids if ids_in is None else ids_in
+    acc = torch.zeros(layer.E_local, dtype=torch.int64, device=dev)
+    hist = torch.zeros((cfg.E, cfg.E), dtype=torch.int64, device=dev)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_track = 50
+    for i in range(n_track + 5):
+        if i == 5:
+            r0.record(stream)
+        L.moe_count_accumulate(b.counts, layer.E_local, acc)
+        L.moe_coactivation(ids_all, T, cfg.k, cfg.E, hist)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    track_us = r0.elapsed_time(r1) / n_track * 1e3
+    hist_h = hist.cpu()
+    G = 8
+    n2o, o2n = torch.empty(cfg.E, dtype=torch.int32), torch.empty(cfg.E, dtype=torch.int32)
+    loads, intra = torch.empty(G, dtype=torch.int64), torch.zeros(1, dtype=torch.int64)
+    h0 = time.perf_counter()
+    L.moe_affinity_partition(torch.diagonal(hist_h).contiguous(), hist_h, cfg.E, G, 20, n2o, o2n,
+                             loads, intra)
+    part_ms = (time.perf_counter() - h0) * 1e3
+    log(f"[bench] rebalance tracking {track_us:.2f} us/step, host affinity partition "
+        f"{part_ms:.2f} ms")
+
     counts = b.counts.cpu().numpy()
     n_rows = int(b.offsets[-1].item())
     gbytes, hit = alg_bytes_gate_up(cfg, layer, counts, n_rows)
@@ -369,6 +396,10 @@ def main():
                            "hbm_GBs": round(lbytes / (ms / 1e3) / 1e9, 1),
                            "tflops": round(lflops / (ms / 1e3) / 1e12, 2)},
         "cpu_baseline": None,
+        "rebalance": {"track_us_per_step": round(track_us, 2),
+                      "track_frac_of_step": round(track_us / 1e3 / ms, 5),
+                      "affinity_partition_host_ms": round(part_ms, 3),
+                      "partition": f"E={cfg.E} into {G} sets, load cap +2%"},
     }
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)

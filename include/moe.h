@@ -191,6 +191,41 @@ moe_status moe_balanced_partition(const int64_t* counts, int E, int G, int32_t* 
 moe_status moe_gather_rows(const void* src, int n_src_rows, void* dst, const int32_t* index,
                            int n_rows, size_t row_bytes, void* stream);
 
+/* Online rebalancing: the measurements the partition works from, kept on the
+ * device across steps ([Moreh-EP] Inter-GPU load balancing: re-measure the
+ * activation frequencies periodically and derive a new expert order;
+ * [SGLang-H20] Expert Affinity EPLB: track top-k co-activation in an expert
+ * affinity matrix).
+ *
+ * moe_count_accumulate: acc[i] += counts[i] for i < n (counts as written by
+ * moe_permute). counts [n] int32 and acc [n] int64 are device memory; acc is
+ * never cleared by the library.
+ *
+ * moe_coactivation: adds one step's top-k picks to an [E][E] int64 histogram
+ * in device memory. For every token, each pick with 0 <= id < E adds 1 to
+ * hist[id][id]; each pair of its picks i < j with valid, distinct ids adds 1
+ * to hist[a][b] and to hist[b][a]; other ids are ignored. Integer atomics:
+ * the result does not depend on the order of the additions. topk_ids [T,k]
+ * int32 device memory. Limits: 1 <= E <= 1024, 1 <= k <= 256, T <= 2^24. */
+moe_status moe_count_accumulate(const int32_t* counts, int n, int64_t* acc, void* stream);
+moe_status moe_coactivation(const int32_t* topk_ids, int T, int k, int E, int64_t* hist,
+                            void* stream);
+
+/* Host-only affinity-aware partition ([SGLang-H20] Expert Affinity EPLB:
+ * co-activated experts placed in the same set; the page gives no algorithm,
+ * this is the reading). Starts from moe_balanced_partition, whose largest set
+ * load is L; allows set loads up to cap = floor(L * (1000 + tol_permille) /
+ * 1000); then repeatedly applies the swap of experts a < b in different sets
+ * that keeps both loads <= cap and raises the total intra-set affinity
+ * (sum over sets of aff[a][b] for a < b in the set) the most, the first such
+ * (a, b) in ascending order on ties, until none raises it (at most 10*E
+ * swaps). aff [E][E] int64 host memory, symmetric (the diagonal is unused);
+ * other arguments as moe_balanced_partition, plus intra_affinity (out, the
+ * final total). tol_permille >= 0. */
+moe_status moe_affinity_partition(const int64_t* counts, const int64_t* aff, int E, int G,
+                                  int tol_permille, int32_t* new_to_old, int32_t* old_to_new,
+                                  int64_t* group_loads, int64_t* intra_affinity);
+
 const char* moe_status_string(moe_status s);
 /* detail of the last error on the calling thread ("" if none) */
 const char* moe_last_error_message(void);

@@ -23,6 +23,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 EXPORTS = [
     "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
     "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_balanced_partition", "moe_gather_rows",
+    "moe_count_accumulate", "moe_coactivation", "moe_affinity_partition",
     "moe_status_string", "moe_last_error_message",
 ]
 
@@ -65,12 +66,16 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [p, i, p, p, i, i, i, p, i, p, i, p]
         L.moe_balanced_partition.argtypes = [p, i, i, p, p, p]
         L.moe_gather_rows.argtypes = [p, i, p, p, i, sz, p]
+        L.moe_count_accumulate.argtypes = [p, i, p, p]
+        L.moe_coactivation.argtypes = [p, i, i, i, p, p]
+        L.moe_affinity_partition.argtypes = [p, p, i, i, i, p, p, p, p]
         L.moe_status_string.argtypes = [i]
         L.moe_status_string.restype = C.c_char_p
         L.moe_last_error_message.restype = C.c_char_p
         for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_gate_up",
                   "moe_expert_ffn_down", "moe_combine",
-                  "moe_balanced_partition", "moe_gather_rows"):
+                  "moe_balanced_partition", "moe_gather_rows", "moe_count_accumulate",
+                  "moe_coactivation", "moe_affinity_partition"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -178,3 +183,25 @@ def moe_balanced_partition(counts, E, G, new_to_old, old_to_new, group_loads):
 def moe_gather_rows(src, n_src_rows, dst, index, n_rows, row_bytes, stream=None):
     _check("moe_gather_rows", lib().moe_gather_rows(_ptr(src), n_src_rows, _ptr(dst), _ptr(index),
                                                     n_rows, row_bytes, _stream(stream)))
+
+
+def moe_count_accumulate(counts, n, acc, stream=None):
+    """acc[i] += counts[i] on the device (int32 counts, int64 acc)."""
+    _check("moe_count_accumulate", lib().moe_count_accumulate(_ptr(counts), n, _ptr(acc),
+                                                              _stream(stream)))
+
+
+def moe_coactivation(topk_ids, T, k, E, hist, stream=None):
+    """Adds one step's picks to the [E, E] int64 co-activation histogram."""
+    _check("moe_coactivation", lib().moe_coactivation(_ptr(topk_ids), T, k, E, _ptr(hist),
+                                                      _stream(stream)))
+
+
+def moe_affinity_partition(counts, aff, E, G, tol_permille, new_to_old, old_to_new, group_loads,
+                           intra_affinity):
+    """Host call: CPU tensors (int64 counts/aff/loads/intra_affinity[1], int32 maps)."""
+    for t in (counts, aff, new_to_old, old_to_new, group_loads, intra_affinity):
+        assert t.device.type == "cpu" and t.is_contiguous()
+    _check("moe_affinity_partition", lib().moe_affinity_partition(
+        _ptr(counts), _ptr(aff), E, G, tol_permille, _ptr(new_to_old), _ptr(old_to_new),
+        _ptr(group_loads), _ptr(intra_affinity)))

@@ -247,6 +247,41 @@ moe_status moe_balanced_partition(const int64_t* counts, int E, int G, int32_t* 
     return balanced_partition(counts, E, G, new_to_old, old_to_new, group_loads);
 }
 
+moe_status moe_count_accumulate(const int32_t* counts, int n, int64_t* acc, void* stream) {
+    g_msg[0] = 0;
+    REQUIRE(n >= 0, MOE_ERR_INVALID_ARG, "moe_count_accumulate: n < 0");
+    if (n == 0) return MOE_OK;
+    REQUIRE(counts && acc, MOE_ERR_INVALID_ARG, "moe_count_accumulate: null pointer");
+    return launch_count_accumulate(counts, n, acc, (hipStream_t)stream);
+}
+
+moe_status moe_coactivation(const int32_t* topk_ids, int T, int k, int E, int64_t* hist,
+                            void* stream) {
+    g_msg[0] = 0;
+    REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "moe_coactivation: T < 0");
+    REQUIRE(T <= (1 << 24), MOE_ERR_UNSUPPORTED, "moe_coactivation: T=%d above 2^24", T);
+    REQUIRE(k >= 1 && k <= 256, MOE_ERR_UNSUPPORTED, "moe_coactivation: k=%d outside [1, 256]", k);
+    REQUIRE(E >= 1 && E <= 1024, MOE_ERR_UNSUPPORTED, "moe_coactivation: E=%d outside [1, 1024]", E);
+    if (T == 0) return MOE_OK;
+    REQUIRE(topk_ids && hist, MOE_ERR_INVALID_ARG, "moe_coactivation: null pointer");
+    return launch_coactivation(topk_ids, T, k, E, hist, (hipStream_t)stream);
+}
+
+moe_status moe_affinity_partition(const int64_t* counts, const int64_t* aff, int E, int G,
+                                  int tol_permille, int32_t* new_to_old, int32_t* old_to_new,
+                                  int64_t* group_loads, int64_t* intra_affinity) {
+    g_msg[0] = 0;
+    REQUIRE(counts && aff && new_to_old && old_to_new && group_loads && intra_affinity,
+            MOE_ERR_INVALID_ARG, "moe_affinity_partition: null pointer");
+    REQUIRE(E >= 1 && G >= 1 && E % G == 0, MOE_ERR_INVALID_ARG,
+            "moe_affinity_partition: need E %% G == 0 (E=%d G=%d)", E, G);
+    REQUIRE(tol_permille >= 0, MOE_ERR_INVALID_ARG, "moe_affinity_partition: tol_permille < 0");
+    for (int e = 0; e < E; ++e)
+        REQUIRE(counts[e] >= 0, MOE_ERR_INVALID_ARG, "moe_affinity_partition: counts[%d] < 0", e);
+    return affinity_partition(counts, aff, E, G, tol_permille, new_to_old, old_to_new, group_loads,
+                              intra_affinity);
+}
+
 moe_status moe_gather_rows(const void* src, int n_src_rows, void* dst, const int32_t* index,
                            int n_rows, size_t row_bytes, void* stream) {
     g_msg[0] = 0;

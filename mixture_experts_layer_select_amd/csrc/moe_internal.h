@@ -89,5 +89,12 @@ moe_status launch_gather_rows(const void* src, void* dst, const int32_t* index, 
 
 moe_status balanced_partition(const int64_t* counts, int E, int G, int32_t* new_to_old,
                               int32_t* old_to_new, int64_t* group_loads);
+moe_status affinity_partition(const int64_t* counts, const int64_t* aff, int E, int G,
+                              int tol_permille, int32_t* new_to_old, int32_t* old_to_new,
+                              int64_t* group_loads, int64_t* intra_affinity);
+
+moe_status launch_count_accumulate(const int32_t* counts, int n, int64_t* acc, hipStream_t st);
+moe_status launch_coactivation(const int32_t* ids, int T, int k, int E, int64_t* hist,
+                               hipStream_t st);
 
 }  // namespace moe

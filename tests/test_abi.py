@@ -126,3 +126,64 @@ def test_balanced_partition_rejects(L):
     c[4] = -1
     _expect(L, L.moe_balanced_partition, "MOE_ERR_INVALID_ARG", c, 10, 2, n2o, o2n,
             torch.empty(2, dtype=torch.int64))
+
+
+def _clustered_ids(rng, T, k, E, n_clusters):
+    """Top-k picks drawn mostly from one of n_clusters expert blocks per
+    token, so the co-activation matrix has structure to find."""
+    blk = E // n_clusters
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        c = rng.integers(n_clusters)
+        own = rng.permutation(blk)[: k - 2] + c * blk
+        rest = np.setdiff1d(np.arange(E), own)
+        ids[t] = np.concatenate([own, rng.choice(rest, 2, replace=False)])
+    return ids
+
+
+@pytest.mark.parametrize("E,G,tol,seed", [(16, 4, 100, 0), (64, 8, 50, 1), (256, 8, 20, 2),
+                                          (256, 8, 0, 3), (12, 3, 1000, 4), (48, 1, 30, 5)])
+def test_affinity_partition_matches_oracle(L, orc, E, G, tol, seed):
+    """The library's incremental swap search against the oracle's direct one:
+    identical maps, loads and intra-set affinity (same swaps, same ties)."""
+    rng = np.random.default_rng(seed)
+    ids = _clustered_ids(rng, 40 * E, min(8, E // G), E, max(G, 2))
+    aff = orc.coactivation(ids, E)
+    counts = np.diag(aff).copy()
+    n2o = torch.empty(E, dtype=torch.int32)
+    o2n = torch.empty(E, dtype=torch.int32)
+    loads = torch.empty(G, dtype=torch.int64)
+    intra = torch.zeros(1, dtype=torch.int64)
+    L.moe_affinity_partition(torch.from_numpy(counts), torch.from_numpy(aff), E, G, tol, n2o, o2n,
+                             loads, intra)
+    r_n2o, r_o2n, r_loads, r_intra = orc.affinity_partition(counts, aff, G, tol)
+    assert np.array_equal(n2o.numpy(), r_n2o)
+    assert np.array_equal(o2n.numpy(), r_o2n)
+    assert np.array_equal(loads.numpy(), r_loads)
+    assert int(intra[0]) == r_intra
+
+
+def test_affinity_partition_rejects(L):
+    E = 8
+    c = torch.ones(E, dtype=torch.int64)
+    a = torch.zeros(E * E, dtype=torch.int64)
+    n2o, o2n = torch.empty(E, dtype=torch.int32), torch.empty(E, dtype=torch.int32)
+    loads, intra = torch.empty(3, dtype=torch.int64), torch.zeros(1, dtype=torch.int64)
+    _expect(L, L.moe_affinity_partition, "MOE_ERR_INVALID_ARG", c, a, E, 3, 0, n2o, o2n, loads,
+            intra)
+    _expect(L, L.moe_affinity_partition, "MOE_ERR_INVALID_ARG", c, a, E, 2, -1, n2o, o2n, loads,
+            intra)
+    c[2] = -5
+    _expect(L, L.moe_affinity_partition, "MOE_ERR_INVALID_ARG", c, a, E, 2, 0, n2o, o2n, loads,
+            intra)
+
+
+def test_rebalance_device_calls_check_arguments(L):
+    _expect(L, L.moe_coactivation, "MOE_ERR_UNSUPPORTED", 1, 4, 0, 8, 1, 0)
+    _expect(L, L.moe_coactivation, "MOE_ERR_UNSUPPORTED", 1, 4, 8, 1025, 1, 0)
+    _expect(L, L.moe_coactivation, "MOE_ERR_INVALID_ARG", 1, -1, 8, 16, 1, 0)
+    _expect(L, L.moe_coactivation, "MOE_ERR_UNSUPPORTED", 1, (1 << 24) + 1, 8, 16, 1, 0)
+    _expect(L, L.moe_coactivation, "MOE_ERR_INVALID_ARG", None, 4, 8, 16, 1, 0)
+    _expect(L, L.moe_count_accumulate, "MOE_ERR_INVALID_ARG", 1, -2, 1, 0)
+    L.moe_coactivation(None, 0, 8, 16, None, 0)  # nothing to add: no device call
+    L.moe_count_accumulate(None, 0, None, 0)
