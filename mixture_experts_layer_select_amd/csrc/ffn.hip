@@ -18,7 +18,11 @@
 //   register ring per wave, activations through a 3-stage LDS ring filled by
 //   direct global->LDS loads.
 // fp8, larger groups (ffn_gemm_fp8_big_kernel, a second launch): 256 x 256
-//   tiles with both operands through a 2-stage LDS ring, MFMA-bound.
+//   tiles with both operands through a 2-stage LDS ring (buffer loads into
+//   LDS), MFMA-bound. Items go in panels of 4 m-tiles x all n-blocks, so the
+//   workgroups of one XCD share both operands' K slices through L2; inside a
+//   K step each 16-token block's operand is read from LDS one block ahead and
+//   the fp32 scaling of each product runs under the next MFMA.
 // fp8 MFMAs are v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales, one
 //   per K step of 128 = one 128x128 weight block and one 1x128 activation
 //   block; the fp32 block scales multiply each partial product.
@@ -145,15 +149,27 @@ __device__ __forceinline__ MTile tile_at(const TileMap& tm, const int32_t* __res
 // consecutive: workgroups that run side by side on one XCD then read that
 // n-block's weights once from HBM and share them through the XCD's L2. A
 // group owns items [start[g]*NB, start[g+1]*NB) in this order as well.
+// With panel > 0 a group's items go in panels of `panel` m-tiles (the last
+// panel may be shorter): all n-blocks of a panel, its m-tiles fastest. The
+// workgroups of one XCD then run a few m-tiles x several n-blocks at once, so
+// each K step's activation slice and weight slice are both shared through L2.
 __device__ __forceinline__ MTile item_at(const TileMap& tm, const int32_t* __restrict__ offsets,
                                          int n_groups, int max_rows, int item, int NB, int bm,
-                                         int& nb) {
+                                         int& nb, int panel = 0) {
     const int g = group_of(tm, n_groups, item / NB);
     const int t0 = tm.start[g];
     const int tg = tm.start[g + 1] - t0;
     const int local = item - t0 * NB;
-    nb = __builtin_amdgcn_readfirstlane(local / tg);
-    return make_tile(tm, offsets, max_rows, g, t0 + local % tg, bm);
+    if (panel <= 0 || tg <= panel) {
+        nb = __builtin_amdgcn_readfirstlane(local / tg);
+        return make_tile(tm, offsets, max_rows, g, t0 + local % tg, bm);
+    }
+    const int full = tg / panel;
+    const int pi = min(local / (panel * NB), full);
+    const int ph = pi < full ? panel : tg - full * panel;
+    const int idx = local - pi * panel * NB;
+    nb = __builtin_amdgcn_readfirstlane(idx / ph);
+    return make_tile(tm, offsets, max_rows, g, t0 + pi * panel + idx % ph, bm);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -432,7 +448,20 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
 __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
 }
+// the same through a buffer descriptor: a 32-bit lane offset plus a uniform
+// offset in a scalar register, no 64-bit address per lane
+__device__ __forceinline__ void lds_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          void* l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff,
+                                             soff, 0, 0);
+}
+__device__ __forceinline__ void lds_buf4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         void* l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 4, voff,
+                                             soff, 0, 0);
+}
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) * 16; }
+
 
 template <bool kSwiGLU>
 __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
@@ -735,6 +764,10 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
 // c ^ ((q >> 1) & 7).
 constexpr int kGTM = 256;  // tokens per tile
 constexpr int kGTN = 256;  // weight rows per tile
+#ifndef MOE_GPANEL
+#define MOE_GPANEL 4
+#endif
+constexpr int kGPanel = MOE_GPANEL;  // m-tiles per item panel
 
 struct BigStage {
     uint8_t w[kGTN * kBK];  // 32 KB
@@ -755,7 +788,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
     __shared__ float red[kSwiGLU ? 4 * kGTM : 1];  // SwiGLU row amax per weight quarter
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int wm = wave & 1;
@@ -768,8 +801,14 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
     const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
 
     for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
-        int nb;
-        const MTile tile = item_at(tm, offsets, n_groups, max_rows, item, NB, kGTM, nb);
+        int nb_v;
+        const MTile tile_v = item_at(tm, offsets, n_groups, max_rows, item, NB, kGTM, nb_v, kGPanel);
+        // the item is the same for every lane: scalar registers, and scalar
+        // branches on the tile's height
+        const int nb = __builtin_amdgcn_readfirstlane(nb_v);
+        const MTile tile{__builtin_amdgcn_readfirstlane(tile_v.group),
+                         __builtin_amdgcn_readfirstlane(tile_v.row0),
+                         __builtin_amdgcn_readfirstlane(tile_v.rows)};
         const bool routed = tile.group < n_routed;
         const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
         const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
@@ -788,7 +827,11 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         // time, so one lane offset of each kind stays live through the loop
         const int q0 = wave * 8 + (lane >> 3);
         const int c16 = ((lane & 7) ^ ((q0 >> 1) & 7)) * 16;
-        const uint8_t* Xt = X + (size_t)tile.row0 * K;
+        const __amdgpu_buffer_rsrc_t wr_d = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K));
+        const __amdgpu_buffer_rsrc_t xr_d =
+            buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K));
+        const __amdgpu_buffer_rsrc_t sr_d = buffer_rsrc(
+            Xs + tile.row0, clamp_bytes(((size_t)(nk - 1) * max_rows + tile.rows) * 4));
         const uint32_t woff0 = (uint32_t)(kSwiGLU ? nb * 128 + q0 : nb * 256 + q0) * K + c16;
         auto wdist = [&](int i) -> uint32_t {  // uniform: piece i's weight row - piece 0's
             if (kSwiGLU) return (uint32_t)(i < 2 ? 64 * i : Nw / 2 + 64 * (i - 2)) * K;
@@ -796,24 +839,22 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         };
         // scales: waves 0..3 load rows 64w + lane (clamped to the tile)
         const int sr = 64 * wave + lane;
-        const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1);
-        const float* Xst = Xs + tile.row0;
+        const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1) * 4;
         const bool s_on = wave < 4 && 64 * wave < tile.rows;
         const int nms = max(0, min(8, (tile.rows - wm * 128 + 15) >> 4));
 
         auto issue = [&](int kc, BigStage& S) {
-            const uint8_t* wk = Wg + (size_t)kc * kBK;
-            const uint8_t* xk = Xt + (size_t)kc * kBK;
+            const uint32_t ko = (uint32_t)kc * kBK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(wk + wdist(i) + woff0, &S.w[(i * 8 + wave) * 1024]);
+            for (int i = 0; i < 4; ++i) lds_buf16(wr_d, woff0, wdist(i) + ko, &S.w[(i * 8 + wave) * 1024]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (64 * i + 8 * wave < tile.rows) {
                     const int r = q0 + 64 * i;
                     const uint32_t xo = (uint32_t)(r < tile.rows ? r : tile.rows - 1) * K + c16;
-                    lds_dma16(xk + xo, &S.x[(i * 8 + wave) * 1024]);
+                    lds_buf16(xr_d, xo, ko, &S.x[(i * 8 + wave) * 1024]);
                 }
-            if (s_on) lds_dma4(Xst + (size_t)kc * max_rows + soff, &S.xs[64 * wave]);
+            if (s_on) lds_buf4(sr_d, soff, (uint32_t)kc * max_rows * 4, &S.xs[64 * wave]);
         };
 
         f32x4 acc[4][8];
@@ -825,6 +866,17 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         // activation row wm*128 + 16ms + li: its swizzle depends on li only
         const int bo0 = (wm * 128 + li) * kBK + ((lk ^ ((li >> 1) & 7)) << 4);
         const int bo1 = (wm * 128 + li) * kBK + (((lk + 4) ^ ((li >> 1) & 7)) << 4);
+        auto load_b = [&](const BigStage& S, int ms) {
+            const uint8_t* base = &S.x[ms * 16 * kBK];
+            return __builtin_shufflevector(*reinterpret_cast<const u32x4*>(base + bo0),
+                                           *reinterpret_cast<const u32x4*>(base + bo1), 0, 1, 2, 3,
+                                           4, 5, 6, 7);
+        };
+        // Over the 16-token blocks ms of a K step: block ms+1's activation
+        // fragment is read from LDS while block ms's MFMAs run, and each
+        // product is scaled into its accumulator while the next MFMA runs.
+        // Rows past the tile read stale LDS bytes whose products are never
+        // kept (ms < nms guards the MFMAs).
         auto compute = [&](int kc, const BigStage& S) {
             if (nms == 0) return;
             u32x8 a[4];
@@ -836,29 +888,44 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
                                                *reinterpret_cast<const u32x4*>(row + swz(q, lk + 4)),
                                                0, 1, 2, 3, 4, 5, 6, 7);
             }
-            // constant first index: the compiler keeps the table apart from the ring
+            // constant first index: the compiler keeps the table apart from the ring.
+            // Weight scale of block s: SwiGLU g0 for gate (s < 2), g1 for up;
+            // down: one block per wave pair
             const float g0 = wsc[0][kc], g1 = wsc[1][kc];
-            float sw[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) sw[s] = kSwiGLU ? ((s >> 1) ? g1 : g0) : ((wn >> 1) ? g1 : g0);
+            const float gd = (wn >> 1) ? g1 : g0;
+            auto wsc_of = [&](int s) { return kSwiGLU ? ((s >> 1) ? g1 : g0) : gd; };
+            u32x8 bb[8];
+            float sxb[8];
+            bb[0] = load_b(S, 0);
+            sxb[0] = S.xs[wm * 128 + li];
 #pragma unroll
             for (int ms = 0; ms < 8; ++ms) {
                 if (ms < nms) {
-                    const uint8_t* base = &S.x[ms * 16 * kBK];
-                    const u32x8 b = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(base + bo0),
-                                                            *reinterpret_cast<const u32x4*>(base + bo1),
-                                                            0, 1, 2, 3, 4, 5, 6, 7);
-                    const float sx = S.xs[wm * 128 + ms * 16 + li];
+                    if (ms + 1 < 8) {
+                        bb[ms + 1] = load_b(S, ms + 1);
+                        sxb[ms + 1] = S.xs[wm * 128 + (ms + 1) * 16 + li];
+                    }
+                    const float f_lo = wsc_of(0) * sxb[ms], f_hi = wsc_of(2) * sxb[ms];
                     f32x4 p[4];
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        p[s] = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, b));
+                        p[s] = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, bb[ms]));
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        const float f = sw[s] * sx;
+                        const float f = s < 2 ? f_lo : f_hi;
 #pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) acc[s][ms][r4] = __builtin_fmaf(p[s][r4], f, acc[s][ms][r4]);
+                        for (int r4 = 0; r4 < 4; ++r4)
+                            acc[s][ms][r4] = __builtin_fmaf(p[s][r4], f, acc[s][ms][r4]);
                     }
+                    // order: the next block's LDS reads, then MFMA 0, MFMA 1,
+                    // scaling of 0, MFMA 2, of 1, MFMA 3, of 2, of 3
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
