@@ -7,7 +7,7 @@
 // persistent grid walks the (m-tile, n-block) work items. Every workgroup
 // builds the tile map in LDS from the offsets, so there is no host sync.
 //
-// bf16 (ffn_gemm_bf16_kernel): 64-row m-tiles, 4 waves. The activation tile
+// bf16 (ffn_gemm_bf16_kernel): 64-row m-tiles, 4 or 8 waves. The activation tile
 //   of each K step (128) is staged in LDS, double buffered, and shared by the
 //   waves; each wave streams its own weight rows from HBM into registers one
 //   step ahead of v_mfma_f32_16x16x32_bf16. Weights are the A operand (16 rows
@@ -42,7 +42,6 @@ constexpr int kBigTile = 64;  // rows per m-tile of the bf16 kernels (128 measur
 #endif
 constexpr int kBf16Occ = MOE_BF16_OCC;  // waves per SIMD the bf16 GEMMs are compiled for
 constexpr int kBK = 128;     // K per step
-constexpr int kThreads = 256;
 
 // m-tiles: group g's rows [offsets[g], offsets[g+1]) split into tiles of at
 // most bm rows (the kernel's tile height); tiles are numbered group after
@@ -232,8 +231,12 @@ __device__ __forceinline__ void barrier_only() {
     __builtin_amdgcn_s_barrier();
 }
 
-template <bool kSwiGLU, int kTM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16Occ, kBf16Occ))) void ffn_gemm_bf16_kernel(
+// kW waves per workgroup: 4, or 8 (an item covers twice the weight rows and
+// the activation tile, staged by waves 0..3, is shared by twice as many
+// waves, so activations are re-read from L2 half as often; the launcher takes
+// it when groups are many and small, where there are items enough for it)
+template <bool kSwiGLU, int kTM, int kW>
+__global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Occ, kBf16Occ))) void ffn_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const uint16_t* __restrict__ Ws,
     int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
     int NB, uint16_t* __restrict__ out, int ldo) {
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
     __shared__ TileMap tm;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;  // (a readfirstlane here measured 10% slower on c5)
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int nk = K / kBK;
@@ -264,10 +267,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
         const uint16_t* Wg = tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
         int ra, rb;
         if (kSwiGLU) {
-            ra = nb * 64 + 16 * wave + li;
+            ra = nb * 16 * kW + 16 * wave + li;
             rb = ra + Nw / 2;
         } else {
-            ra = nb * 128 + 32 * wave + li;
+            ra = nb * 32 * kW + 32 * wave + li;
             rb = ra + 16;
         }
         // buffer loads: 32-bit lane offsets against a scalar descriptor, so no
@@ -352,24 +355,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
         // ring measured faster than 3-deep at two workgroups per CU), compute
         // j, wait for the activations only (the 8 weight loads stay in flight),
         // stage them, barrier
+        // waves 0..3 stage the activation tile; waves past them issue only their
+        // 8 weight loads a step, so vmcnt(8) does not wait for those either
+        const bool stager = kW == 4 || wave < 4;
         auto step = [&](int j, auto cur, auto nxt) {
-            load_x(j + 1);
+            if (stager) load_x(j + 1);
             load_w(j + 1, nxt);
             __builtin_amdgcn_sched_barrier(0);
             compute(j & 1, cur);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<8>();
-            store_x((j + 1) & 1);
+            if (stager) store_x((j + 1) & 1);
             barrier_only();
         };
 
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
         // prologue: activations and weights of step 0
-        load_x(0);
+        if (stager) load_x(0);
         load_w(0, S0{});
         wait_vmcnt<8>();  // the activations (issued first) have landed
-        store_x(0);
+        if (stager) store_x(0);
         barrier_only();
         for (int j = 0;; j += 2) {
             step(j, S0{}, S1{});
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
             if (ms < nms && m < tile.rows) {
                 uint16_t* orow = out + (size_t)(tile.row0 + m) * ldo;
                 if (kSwiGLU) {
-                    const int col = nb * 64 + 16 * wave + 4 * lk;
+                    const int col = nb * 16 * kW + 16 * wave + 4 * lk;
                     float a0 = silu_mul(acc_a[ms][0], acc_b[ms][0]);
                     float a1 = silu_mul(acc_a[ms][1], acc_b[ms][1]);
                     float a2 = silu_mul(acc_a[ms][2], acc_b[ms][2]);
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBf16O
                     *reinterpret_cast<uint2*>(orow + col) =
                         make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3));
                 } else {
-                    const int col = nb * 128 + 32 * wave + 4 * lk;
+                    const int col = nb * 32 * kW + 32 * wave + 4 * lk;
                     *reinterpret_cast<uint2*>(orow + col) =
                         make_uint2(pack_bf16x2(acc_a[ms][0], acc_a[ms][1]),
                                    pack_bf16x2(acc_a[ms][2], acc_a[ms][3]));
@@ -1068,6 +1074,14 @@ FfnWs carve(const moe_expert_weights* w, int max_rows, void* base) {
     return r;
 }
 
+// 8-wave bf16 workgroups when the groups are many and small (at most 32
+// rows per group on average over the buffer bound, as in decode with all
+// experts local): items stay plentiful at twice the width. Otherwise, or when
+// H is not a multiple of 256 (the down GEMM's 256-row n-blocks), 4 waves.
+bool bf16_wide(const moe_expert_weights* w, int max_rows, int n_groups) {
+    return w->H % 256 == 0 && w->I % 128 == 0 && max_rows <= 32L * n_groups;
+}
+
 int persistent_grid(long bound, int per_cu) {
     const long cap = (long)device_info().cu_count * per_cu;
     long g = bound < cap ? bound : cap;
@@ -1099,12 +1113,20 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
         return check_launch("ffn_gemm1_f32_kernel");
     }
     if (w->dt == MOE_BF16) {
-        const int NB = I / 64;
-        const long tiles128 = (long)(max_rows + kBigTile - 1) / kBigTile + n_groups;
-        hipLaunchKernelGGL((ffn_gemm_bf16_kernel<true, kBigTile>), dim3(persistent_grid_xcd(tiles128 * NB, kBf16Occ)),
-                           dim3(kThreads), 0, st, (const uint16_t*)x_perm, (const uint16_t*)w->w13,
-                           (const uint16_t*)w->ws13, E, offsets, n_groups, max_rows, H, 2 * I, NB,
-                           (uint16_t*)s.a, I);
+        const long tiles = (long)(max_rows + kBigTile - 1) / kBigTile + n_groups;
+        if (bf16_wide(w, max_rows, n_groups)) {
+            const int NB = I / (16 * 8);
+            hipLaunchKernelGGL((ffn_gemm_bf16_kernel<true, kBigTile, 8>),
+                               dim3(persistent_grid_xcd(tiles * NB, kBf16Occ / 2)), dim3(8 * 64), 0, st,
+                               (const uint16_t*)x_perm, (const uint16_t*)w->w13, (const uint16_t*)w->ws13,
+                               E, offsets, n_groups, max_rows, H, 2 * I, NB, (uint16_t*)s.a, I);
+        } else {
+            const int NB = I / (16 * 4);
+            hipLaunchKernelGGL((ffn_gemm_bf16_kernel<true, kBigTile, 4>),
+                               dim3(persistent_grid_xcd(tiles * NB, kBf16Occ)), dim3(4 * 64), 0, st,
+                               (const uint16_t*)x_perm, (const uint16_t*)w->w13, (const uint16_t*)w->ws13,
+                               E, offsets, n_groups, max_rows, H, 2 * I, NB, (uint16_t*)s.a, I);
+        }
         return check_launch("ffn_gemm_bf16_kernel<gate_up>");
     }
     const int NB = I / 128;
@@ -1140,12 +1162,20 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
         return check_launch("ffn_gemm2_f32_kernel");
     }
     if (w->dt == MOE_BF16) {
-        const int NB = H / 128;
-        const long tiles128 = (long)(max_rows + kBigTile - 1) / kBigTile + n_groups;
-        hipLaunchKernelGGL((ffn_gemm_bf16_kernel<false, kBigTile>), dim3(persistent_grid_xcd(tiles128 * NB, kBf16Occ)),
-                           dim3(kThreads), 0, st, (const uint16_t*)s.a, (const uint16_t*)w->w2,
-                           (const uint16_t*)w->ws2, E, offsets, n_groups, max_rows, I, H, NB,
-                           (uint16_t*)y_perm, H);
+        const long tiles = (long)(max_rows + kBigTile - 1) / kBigTile + n_groups;
+        if (bf16_wide(w, max_rows, n_groups)) {
+            const int NB = H / (32 * 8);
+            hipLaunchKernelGGL((ffn_gemm_bf16_kernel<false, kBigTile, 8>),
+                               dim3(persistent_grid_xcd(tiles * NB, kBf16Occ / 2)), dim3(8 * 64), 0, st,
+                               (const uint16_t*)s.a, (const uint16_t*)w->w2, (const uint16_t*)w->ws2, E,
+                               offsets, n_groups, max_rows, I, H, NB, (uint16_t*)y_perm, H);
+        } else {
+            const int NB = H / (32 * 4);
+            hipLaunchKernelGGL((ffn_gemm_bf16_kernel<false, kBigTile, 4>),
+                               dim3(persistent_grid_xcd(tiles * NB, kBf16Occ)), dim3(4 * 64), 0, st,
+                               (const uint16_t*)s.a, (const uint16_t*)w->w2, (const uint16_t*)w->ws2, E,
+                               offsets, n_groups, max_rows, I, H, NB, (uint16_t*)y_perm, H);
+        }
         return check_launch("ffn_gemm_bf16_kernel<down>");
     }
     const int NB = H / 256;

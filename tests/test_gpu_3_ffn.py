@@ -74,6 +74,17 @@ def test_ffn_no_shared_many_small_groups(fmt):
     _run(fmt, 768, 384, sizes, shared=False, seed=1)
 
 
+def test_ffn_bf16_wide_path_mixed_groups():
+    """Many groups averaging a few rows (the launcher's 8-wave bf16 path: at
+    most 32 rows per group over the buffer) with three multi-tile groups among
+    them and the shared group last."""
+    rng = np.random.default_rng(11)
+    sizes = list(rng.integers(0, 7, 57))
+    sizes[5], sizes[20], sizes[41] = 70, 150, 200
+    assert sum(sizes) + 5 <= 32 * (len(sizes) + 1)
+    _run("bf16", 512, 256, sizes + [33], shared=True, seed=6)
+
+
 def test_ffn_fp32_tiny():
     _run("f32", 64, 32, [3, 0, 5, 1, 7], shared=True)
 
