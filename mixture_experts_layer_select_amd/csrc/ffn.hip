@@ -246,7 +246,8 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
     __shared__ TileMap tm;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;  // (a readfirstlane here measured 10% slower on c5)
+    // left per-lane: making it wave-uniform measured 10% slower on a 512-token, 32-expert share
+    const int wave = threadIdx.x >> 6;
     const int li = lane & 15;
     const int lk = lane >> 4;
     const int nk = K / kBK;
