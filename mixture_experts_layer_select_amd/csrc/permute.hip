@@ -169,19 +169,34 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t* __restr
         excl[e] = run;  // count for now
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int g = 0; g < E_local; ++g) {
-            const int c = excl[g];
-            counts[g] = c;
-            offsets[g] = run;
-            excl[g] = run;
-            run += c;
+    {
+        // exclusive scan of the counts over experts: an inclusive scan within
+        // each wave (shuffles), then over the wave totals
+        __shared__ int wave_tot[1024 / 64];
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int c = threadIdx.x < E_local ? excl[threadIdx.x] : 0;
+        int v = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int n = __shfl_up(v, d);
+            if (lane >= d) v += n;
         }
-        counts[E_local] = n_shared;
-        offsets[E_local] = run;
-        offsets[E_local + 1] = run + n_shared;
-        excl[E_local] = run;
+        if (lane == 63) wave_tot[wv] = v;
+        __syncthreads();
+        int before = 0;
+        for (int u = 0; u < wv; ++u) before += wave_tot[u];
+        const int incl = before + v;
+        if (threadIdx.x < E_local) {
+            counts[threadIdx.x] = c;
+            offsets[threadIdx.x] = incl - c;
+            excl[threadIdx.x] = incl - c;
+        }
+        if (threadIdx.x == E_local - 1) {
+            counts[E_local] = n_shared;
+            offsets[E_local] = incl;
+            offsets[E_local + 1] = incl + n_shared;
+            excl[E_local] = incl;
+        }
     }
     __syncthreads();
     const int R = excl[E_local];
