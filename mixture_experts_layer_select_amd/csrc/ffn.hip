@@ -262,39 +262,98 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
     const int i_lo = (int)((long)n_items * xcd / 8);
     const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
 
-    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
+    // per-item addressing: the tile, its weight and activation descriptors and
+    // this lane's offsets into them
+    struct Ctx {
+        MTile tile;
         int nb;
-        const MTile tile = item_at(tm, offsets, n_groups, max_rows, item, NB, kTM, nb);
-        const uint16_t* Wg = tile.group < n_routed ? W + (size_t)tile.group * Nw * K : Ws;
+        __amdgpu_buffer_rsrc_t wr, xr;
+        uint32_t wa, wb;
+        uint32_t xoff[kOwn];
+    };
+    const int xrow0 = 16 * wave + li;  // activation staging: wave w owns tile rows 16(w + 4q) + [0, 16)
+    auto ctx_of = [&](int it) {
+        Ctx c;
+        c.tile = item_at(tm, offsets, n_groups, max_rows, it, NB, kTM, c.nb);
+        const uint16_t* Wg = c.tile.group < n_routed ? W + (size_t)c.tile.group * Nw * K : Ws;
         int ra, rb;
         if (kSwiGLU) {
-            ra = nb * 16 * kW + 16 * wave + li;
+            ra = c.nb * 16 * kW + 16 * wave + li;
             rb = ra + Nw / 2;
         } else {
-            ra = nb * 32 * kW + 32 * wave + li;
+            ra = c.nb * 32 * kW + 32 * wave + li;
             rb = ra + 16;
         }
         // buffer loads: 32-bit lane offsets against a scalar descriptor, so no
         // 64-bit VGPR address temporaries, which the register allocator would
         // otherwise carve out of the weight ring (forcing a wait for the ring's
         // loads before the address is written)
-        const uint32_t wa = ((uint32_t)ra * K + 8 * lk) * 2;
-        const uint32_t wb = ((uint32_t)rb * K + 8 * lk) * 2;
-        const __amdgpu_buffer_rsrc_t wr_d = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K * 2));
-        const int nms = (tile.rows + 15) >> 4;
-
-        // activation staging: wave w owns tile rows 16(w + 4q) + [0, 16), q < kOwn;
-        // lane (li, lk) copies 64 B of each such row (k = 32c + 8lk pieces)
-        int xrow[kOwn];
-        uint32_t xoff[kOwn];
-        const __amdgpu_buffer_rsrc_t xr_d =
-            buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K * 2));
+        c.wa = ((uint32_t)ra * K + 8 * lk) * 2;
+        c.wb = ((uint32_t)rb * K + 8 * lk) * 2;
+        c.wr = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K * 2));
+        c.xr = buffer_rsrc(X + (size_t)c.tile.row0 * K, clamp_bytes((size_t)c.tile.rows * K * 2));
 #pragma unroll
         for (int q = 0; q < kOwn; ++q) {
-            xrow[q] = 16 * (wave + 4 * q) + li;
-            const int xrr = xrow[q] < tile.rows ? xrow[q] : tile.rows - 1;
-            xoff[q] = ((uint32_t)xrr * K + 8 * lk) * 2;
+            const int xrow = xrow0 + 64 * q;
+            const int xrr = xrow < c.tile.rows ? xrow : c.tile.rows - 1;
+            c.xoff[q] = ((uint32_t)xrr * K + 8 * lk) * 2;
         }
+        return c;
+    };
+
+    u32x4 ring[2][2][4];  // weights of steps j (slot j & 1) and j + 1
+    u32x4 xr[kOwn][4];
+    auto load_w = [&](const Ctx& c, int kc, auto slot_c) {
+        constexpr int st = decltype(slot_c)::value;
+        kc = kc < nk ? kc : nk - 1;
+        const uint32_t ko = (uint32_t)kc * kBK * 2;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            ring[st][0][cc] = buffer_load16(c.wr, c.wa + 64 * cc, ko);
+            ring[st][1][cc] = buffer_load16(c.wr, c.wb + 64 * cc, ko);
+        }
+    };
+    auto load_x = [&](const Ctx& c, int kc) {
+        kc = kc < nk ? kc : nk - 1;
+        const uint32_t ko = (uint32_t)kc * kBK * 2;
+#pragma unroll
+        for (int q = 0; q < kOwn; ++q)
+            if (16 * (wave + 4 * q) < c.tile.rows) {  // rows of this wave inside the tile
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) xr[q][cc] = buffer_load16(c.xr, c.xoff[q] + 64 * cc, ko);
+            }
+    };
+    // unconditional: a wave whose rows lie past the tile stores whatever its
+    // registers hold, which no MFMA result that is kept depends on. A
+    // guarded store lets the compiler sink the loads into the guarded
+    // block, behind the weight loads, and then wait for all of them there.
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < kOwn; ++q) {
+            uint8_t* d = &xs[buf][(xrow0 + 64 * q) * kLdsRowBf16];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) *reinterpret_cast<u32x4*>(d + 64 * cc + 16 * lk) = xr[q][cc];
+        }
+    };
+    // waves 0..3 stage the activation tile; waves past them issue only their
+    // 8 weight loads a step, so vmcnt(8) does not wait for those either
+    const bool stager = kW == 4 || wave < 4;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // Across items: the last K step of an item issues the next item's step 0
+    // (into weight slot 0 and LDS buffer 0 when nk is even), so a workgroup's
+    // next item starts with its first operands landed instead of waiting a
+    // full memory latency.
+    const bool chain = (nk & 1) == 0;
+    bool primed = false;  // this item's step 0 was issued by the previous one
+
+    for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
+        const Ctx cur_c = ctx_of(item);
+        const bool has_next = chain && item + per_xcd < i_hi;
+        const Ctx nxt_c = has_next ? ctx_of(item + per_xcd) : cur_c;
+        const MTile tile = cur_c.tile;
+        const int nb = cur_c.nb;
+        const int nms = (tile.rows + 15) >> 4;
 
         f32x4 acc_a[kSub], acc_b[kSub];
 #pragma unroll
@@ -302,41 +361,6 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
             acc_a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc_b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        u32x4 ring[2][2][4];  // weights of steps j (slot j & 1) and j + 1
-        u32x4 xr[kOwn][4];
-
-        auto load_w = [&](int kc, auto slot_c) {
-            constexpr int st = decltype(slot_c)::value;
-            kc = kc < nk ? kc : nk - 1;
-            const uint32_t ko = (uint32_t)kc * kBK * 2;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                ring[st][0][c] = buffer_load16(wr_d, wa + 64 * c, ko);
-                ring[st][1][c] = buffer_load16(wr_d, wb + 64 * c, ko);
-            }
-        };
-        auto load_x = [&](int kc) {
-            kc = kc < nk ? kc : nk - 1;
-            const uint32_t ko = (uint32_t)kc * kBK * 2;
-#pragma unroll
-            for (int q = 0; q < kOwn; ++q)
-                if (16 * (wave + 4 * q) < tile.rows) {  // rows of this wave inside the tile
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) xr[q][c] = buffer_load16(xr_d, xoff[q] + 64 * c, ko);
-                }
-        };
-        // unconditional: a wave whose rows lie past the tile stores whatever its
-        // registers hold, which no MFMA result that is kept depends on. A
-        // guarded store lets the compiler sink the loads into the guarded
-        // block, behind the weight loads, and then wait for all of them there.
-        auto store_x = [&](int buf) {
-#pragma unroll
-            for (int q = 0; q < kOwn; ++q) {
-                uint8_t* d = &xs[buf][xrow[q] * kLdsRowBf16];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(d + 64 * c + 16 * lk) = xr[q][c];
-            }
-        };
         auto compute = [&](int buf, auto slot_c) {
             constexpr int st = decltype(slot_c)::value;
 #pragma unroll
@@ -355,13 +379,13 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
         // one K step: activations of j+1 first, then weights of j+1 (a 2-deep
         // ring measured faster than 3-deep at two workgroups per CU), compute
         // j, wait for the activations only (the 8 weight loads stay in flight),
-        // stage them, barrier
-        // waves 0..3 stage the activation tile; waves past them issue only their
-        // 8 weight loads a step, so vmcnt(8) does not wait for those either
-        const bool stager = kW == 4 || wave < 4;
+        // stage them, barrier. The last step loads the next item's step 0.
         auto step = [&](int j, auto cur, auto nxt) {
-            if (stager) load_x(j + 1);
-            load_w(j + 1, nxt);
+            const bool to_next = has_next && j + 1 >= nk;
+            const Ctx& lc = to_next ? nxt_c : cur_c;
+            const int lk_step = to_next ? 0 : j + 1;
+            if (stager) load_x(lc, lk_step);
+            load_w(lc, lk_step, nxt);
             __builtin_amdgcn_sched_barrier(0);
             compute(j & 1, cur);
             __builtin_amdgcn_sched_barrier(0);
@@ -370,21 +394,21 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
             barrier_only();
         };
 
-        using S0 = std::integral_constant<int, 0>;
-        using S1 = std::integral_constant<int, 1>;
-        // prologue: activations and weights of step 0
-        if (stager) load_x(0);
-        load_w(0, S0{});
-        wait_vmcnt<8>();  // the activations (issued first) have landed
-        if (stager) store_x(0);
-        barrier_only();
+        if (!primed) {  // prologue: activations and weights of step 0
+            if (stager) load_x(cur_c, 0);
+            load_w(cur_c, 0, S0{});
+            wait_vmcnt<8>();  // the activations (issued first) have landed
+            if (stager) store_x(0);
+            barrier_only();
+        }
         for (int j = 0;; j += 2) {
             step(j, S0{}, S1{});
             if (j + 1 >= nk) break;
             step(j + 1, S1{}, S0{});
             if (j + 2 >= nk) break;
         }
-        wait_vmcnt<0>();  // the clamped tail loads land before registers are reused
+        primed = has_next;
+        if (!has_next) wait_vmcnt<0>();  // the clamped tail loads land before registers are reused
 
         // epilogue: lane holds D[n = base + 4*lk + r][m = ms*16 + li]
 #pragma unroll
