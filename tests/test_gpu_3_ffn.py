@@ -105,6 +105,14 @@ def test_ffn_groups_across_the_tile_height(fmt):
     _run(fmt, 512, 256, [0, 257, 3, 513, 256, 700, 1, 0, 600], shared=True, seed=3)
 
 
+def test_ffn_fp8_large_groups_in_panels():
+    """Groups of 6 and 9 256-row tiles (the large-group launch orders a
+    group's items in panels of 4 m-tiles: one full panel and a 2-tile
+    remainder, two full panels and a 1-tile one), a 5-tile group and small
+    groups between them."""
+    _run("fp8", 512, 256, [1300, 7, 2100, 0, 1180, 40], shared=True, seed=7)
+
+
 def test_ffn_fp8_r1_shape_large_group():
     """H=7168, I=2048 with one 300-row expert (two tiles of 150) and a 40-row
     one: the full-size K loops of both fp8 launches."""
