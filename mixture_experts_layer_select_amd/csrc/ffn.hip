@@ -907,7 +907,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         // fragment is read from LDS while block ms's MFMAs run, and each
         // product is scaled into its accumulator while the next MFMA runs.
         // Rows past the tile read stale LDS bytes whose products are never
-        // kept (ms < nms guards the MFMAs).
+        // kept.
         auto compute = [&](int kc, const BigStage& S) {
             if (nms == 0) return;
             u32x8 a[4];
@@ -929,37 +929,57 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
             float sxb[8];
             bb[0] = load_b(S, 0);
             sxb[0] = S.xs[wm * 128 + li];
+            // Every 16-token block is computed: in this launch every tile has
+            // more than 128 rows, so the waves of the first token half (wm = 0)
+            // always run 8 blocks, and the barrier of each K step waits for
+            // them; the second half's blocks past the tile cost no time
+            // (those waves sit on other SIMDs) and their rows are never kept.
+            // The last product of block ms is scaled under block ms+1's first
+            // MFMA, so no scaling waits on the MFMA just issued. Per block:
+            // MFMA 0, (scale factors, scaling of the previous block's product
+            // 3), MFMA 1, scaling of 0, MFMA 2, of 1, MFMA 3, of 2.
+            f32x4 pend;
+            float f_pend = 0.f;
 #pragma unroll
             for (int ms = 0; ms < 8; ++ms) {
-                if (ms < nms) {
-                    if (ms + 1 < 8) {
-                        bb[ms + 1] = load_b(S, ms + 1);
-                        sxb[ms + 1] = S.xs[wm * 128 + (ms + 1) * 16 + li];
-                    }
-                    const float f_lo = wsc_of(0) * sxb[ms], f_hi = wsc_of(2) * sxb[ms];
-                    f32x4 p[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        p[s] = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, bb[ms]));
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float f = s < 2 ? f_lo : f_hi;
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4)
-                            acc[s][ms][r4] = __builtin_fmaf(p[s][r4], f, acc[s][ms][r4]);
-                    }
-                    // order: the next block's LDS reads, then MFMA 0, MFMA 1,
-                    // scaling of 0, MFMA 2, of 1, MFMA 3, of 2, of 3
-                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                if (ms + 1 < 8) {
+                    bb[ms + 1] = load_b(S, ms + 1);
+                    sxb[ms + 1] = S.xs[wm * 128 + (ms + 1) * 16 + li];
                 }
+                f32x4 p[4];
+                p[0] = mfma_fp8(__builtin_bit_cast(i32x8, a[0]), __builtin_bit_cast(i32x8, bb[ms]));
+                const float f_lo = wsc_of(0) * sxb[ms], f_hi = wsc_of(2) * sxb[ms];
+                if (ms > 0) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        acc[3][ms - 1][r4] = __builtin_fmaf(pend[r4], f_pend, acc[3][ms - 1][r4]);
+                }
+#pragma unroll
+                for (int s = 1; s < 4; ++s) {
+                    p[s] = mfma_fp8(__builtin_bit_cast(i32x8, a[s]), __builtin_bit_cast(i32x8, bb[ms]));
+                    const float f = s - 1 < 2 ? f_lo : f_hi;
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        acc[s - 1][ms][r4] = __builtin_fmaf(p[s - 1][r4], f, acc[s - 1][ms][r4]);
+                }
+                pend = p[3];
+                f_pend = f_hi;
+                if (ms + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (ms > 0)
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                else
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) acc[3][7][r4] = __builtin_fmaf(pend[r4], f_pend, acc[3][7][r4]);
         };
 
         issue(0, st0);
