@@ -115,6 +115,70 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 }
 
+// k <= kSmallK with 8-column vectors: the unit's token is the same for the
+// whole workgroup, so its pick rows and weights are uniform loads kept in
+// scalar registers (no LDS staging, no barriers), and the next unit's are
+// loaded before the current unit's rows are summed, so the index latency of
+// one unit hides under the row loads of the previous one. Same summation
+// order as combine_kernel: slots 0..k-1, then the shared row.
+constexpr int kSmallK = 8;
+template <typename TY, typename TO>
+__global__ __launch_bounds__(kCombineThreads) void combine_small_k_kernel(
+    const TY* __restrict__ y, const int32_t* __restrict__ slot_to_row,
+    const float* __restrict__ topk_w, int T, int k, int H, const int32_t* __restrict__ offsets,
+    int shared_group, TO* __restrict__ out) {
+    const int nch = (H + kChunkH - 1) / kChunkH;
+    const long n_units = (long)T * nch;
+    const int shared0 = shared_group >= 0 ? offsets[shared_group] : -1;
+    auto fetch = [&](long u, int* rows, float* wts) {
+        const int t = (int)(u / nch);
+#pragma unroll
+        for (int j = 0; j < kSmallK; ++j) {
+            rows[j] = j < k ? slot_to_row[(size_t)t * k + j] : -1;
+            wts[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+        }
+    };
+    int rows[kSmallK];
+    float wts[kSmallK];
+    long u = blockIdx.x;
+    if (u < n_units) fetch(u, rows, wts);
+    for (; u < n_units; u += gridDim.x) {
+        const int t = (int)(u / nch);
+        const int h = (int)(u % nch) * kChunkH + threadIdx.x * 8;
+        // every row load is issued before the first sum; a non-local pick
+        // (row -1) reads row 0 of y, which the caller's buffer always holds,
+        // and its value is never used
+        float v[kSmallK][8], vs[8];
+        if (h < H) {
+#pragma unroll
+            for (int j = 0; j < kSmallK; ++j) load8(y + (size_t)(rows[j] > 0 ? rows[j] : 0) * H + h, v[j]);
+            load8(y + (size_t)(shared0 >= 0 ? shared0 + t : 0) * H + h, vs);
+        }
+        float wc[kSmallK];
+        int rc[kSmallK];
+#pragma unroll
+        for (int j = 0; j < kSmallK; ++j) {
+            wc[j] = wts[j];
+            rc[j] = rows[j];
+        }
+        if (u + gridDim.x < n_units) fetch(u + gridDim.x, rows, wts);
+        if (h < H) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kSmallK; ++j)
+                if (rc[j] >= 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wc[j], v[j][i], acc[i]);
+                }
+            if (shared0 >= 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += vs[i];
+            }
+            store8(out + (size_t)t * H + h, acc);
+        }
+    }
+}
+
 __global__ void gather_rows_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
                                    const int32_t* __restrict__ index, int n_src_rows, int n_rows,
                                    long row_words) {
@@ -139,6 +203,12 @@ moe_status launch_combine(const void* y_perm, moe_dtype y_dt, const int32_t* slo
                           int shared_group, void* out, moe_dtype out_dt, hipStream_t st) {
     const long units = (long)T * ((H + kChunkH - 1) / kChunkH);
     const int blocks = (int)std::max(1L, std::min(units, (long)device_info().cu_count * 16));
+    if (k <= kSmallK && (H & 7) == 0 && y_dt == MOE_BF16 && out_dt == MOE_BF16) {
+        hipLaunchKernelGGL((combine_small_k_kernel<uint16_t, uint16_t>), dim3(blocks), dim3(kCombineThreads), 0,
+                           st, (const uint16_t*)y_perm, slot_to_row, topk_w, T, k, H, offsets,
+                           shared_group, (uint16_t*)out);
+        return check_launch("combine_small_k_kernel");
+    }
     if (y_dt == MOE_BF16 && out_dt == MOE_BF16)
         hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), dim3(blocks), dim3(kCombineThreads), 0, st,
                            (const uint16_t*)y_perm, slot_to_row, topk_w, T, k, H, offsets,

@@ -260,31 +260,47 @@ __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
     const long used = offsets[E_local + 1];
     const int nb = H / 128;
     const int sub = threadIdx.x & 15;
-    for (long r = blockIdx.x; r < used; r += gridDim.x) {
-        const long t = token_of(row_to_slot[r], S, k);
+    // 16 threads per 128-column block, 16 blocks per pass; a pass of four
+    // rounds issues all of its row loads before the first block is quantised,
+    // and the next row's token index is loaded before this row's work
+    long r = blockIdx.x;
+    int32_t slot = r < used ? row_to_slot[r] : 0;
+    for (; r < used; r += gridDim.x) {
+        const long t = token_of(slot, S, k);
+        if (r + gridDim.x < used) slot = row_to_slot[r + gridDim.x];
         const uint16_t* src = x + t * H;
-        for (int b = threadIdx.x >> 4; b < nb; b += 16) {
-            const int h0 = b * 128 + sub * 8;
-            u32x4 q = *reinterpret_cast<const u32x4*>(src + h0);
-            float v[8];
+        for (int b0 = threadIdx.x >> 4; b0 < nb; b0 += 64) {
+            u32x4 q[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                v[2 * i] = bf16_lo(q[i]);
-                v[2 * i + 1] = bf16_hi(q[i]);
+                const int b = b0 + 16 * i;
+                if (b < nb) q[i] = *reinterpret_cast<const u32x4*>(src + b * 128 + sub * 8);
             }
-            float a = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+            for (int i = 0; i < 4; ++i) {
+                const int b = b0 + 16 * i;
+                if (b >= nb) break;
+                const int h0 = b * 128 + sub * 8;
+                float v[8];
 #pragma unroll
-            for (int s = 8; s >= 1; s >>= 1) a = fmaxf(a, __shfl_xor(a, s));
-            const float sc = block_scale(a);
-            float qv[8];
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = bf16_lo(q[i][e]);
+                    v[2 * e + 1] = bf16_hi(q[i][e]);
+                }
+                float a = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qv[i] = clamp_e4m3(v[i] / sc);
-            uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
-            uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
-            *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
-            if (sub == 0) x_scale[b * cap + r] = sc;
+                for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+#pragma unroll
+                for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+                const float sc = block_scale(a);
+                float qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[e] = clamp_e4m3(v[e] / sc);
+                const uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
+                const uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
+                *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
+                if (sub == 0) x_scale[b * cap + r] = sc;
+            }
         }
     }
 }
