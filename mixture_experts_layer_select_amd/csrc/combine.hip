@@ -115,18 +115,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     }
 }
 
-// k <= kSmallK with 8-column vectors: the unit's token is the same for the
+// bf16 rows and output, k <= kSmallK, 8-column vectors: the unit's token is the same for the
 // whole workgroup, so its pick rows and weights are uniform loads kept in
 // scalar registers (no LDS staging, no barriers), and the next unit's are
 // loaded before the current unit's rows are summed, so the index latency of
 // one unit hides under the row loads of the previous one. Same summation
 // order as combine_kernel: slots 0..k-1, then the shared row.
 constexpr int kSmallK = 8;
-template <typename TY, typename TO>
 __global__ __launch_bounds__(kCombineThreads) void combine_small_k_kernel(
-    const TY* __restrict__ y, const int32_t* __restrict__ slot_to_row,
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_to_row,
     const float* __restrict__ topk_w, int T, int k, int H, const int32_t* __restrict__ offsets,
-    int shared_group, TO* __restrict__ out) {
+    int shared_group, uint16_t* __restrict__ out) {
     const int nch = (H + kChunkH - 1) / kChunkH;
     const long n_units = (long)T * nch;
     const int shared0 = shared_group >= 0 ? offsets[shared_group] : -1;
@@ -145,14 +144,25 @@ __global__ __launch_bounds__(kCombineThreads) void combine_small_k_kernel(
     for (; u < n_units; u += gridDim.x) {
         const int t = (int)(u / nch);
         const int h = (int)(u % nch) * kChunkH + threadIdx.x * 8;
-        // every row load is issued before the first sum; a non-local pick
-        // (row -1) reads row 0 of y, which the caller's buffer always holds,
-        // and its value is never used
+        // every row load is issued before the first sum, each through a
+        // descriptor of its (uniform) row: a non-local pick (row -1) or an
+        // absent shared row gets an empty range, so its load reads zeros
+        // without a memory request and its value is never used
         float v[kSmallK][8], vs[8];
+        auto row_load = [&](int row, float* out8) {
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(y + (size_t)(row > 0 ? row : 0) * H, row >= 0 ? (uint32_t)H * 2u : 0u);
+            const u32x4 q = buffer_load16(rs, (uint32_t)h * 2u, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                out8[2 * i] = bf16_lo(q[i]);
+                out8[2 * i + 1] = bf16_hi(q[i]);
+            }
+        };
         if (h < H) {
 #pragma unroll
-            for (int j = 0; j < kSmallK; ++j) load8(y + (size_t)(rows[j] > 0 ? rows[j] : 0) * H + h, v[j]);
-            load8(y + (size_t)(shared0 >= 0 ? shared0 + t : 0) * H + h, vs);
+            for (int j = 0; j < kSmallK; ++j) row_load(rows[j], v[j]);
+            row_load(shared0 >= 0 ? shared0 + t : -1, vs);
         }
         float wc[kSmallK];
         int rc[kSmallK];
@@ -204,7 +214,7 @@ moe_status launch_combine(const void* y_perm, moe_dtype y_dt, const int32_t* slo
     const long units = (long)T * ((H + kChunkH - 1) / kChunkH);
     const int blocks = (int)std::max(1L, std::min(units, (long)device_info().cu_count * 16));
     if (k <= kSmallK && (H & 7) == 0 && y_dt == MOE_BF16 && out_dt == MOE_BF16) {
-        hipLaunchKernelGGL((combine_small_k_kernel<uint16_t, uint16_t>), dim3(blocks), dim3(kCombineThreads), 0,
+        hipLaunchKernelGGL(combine_small_k_kernel, dim3(blocks), dim3(kCombineThreads), 0,
                            st, (const uint16_t*)y_perm, slot_to_row, topk_w, T, k, H, offsets,
                            shared_group, (uint16_t*)out);
         return check_launch("combine_small_k_kernel");

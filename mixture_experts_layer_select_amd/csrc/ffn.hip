@@ -173,17 +173,6 @@ __device__ __forceinline__ MTile item_at(const TileMap& tm, const int32_t* __res
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Raw buffer access: a 128-bit descriptor in SGPRs (base, size in bytes) plus
-// a 32-bit lane offset and a scalar offset. Loads need no 64-bit VGPR address
-// arithmetic, and accesses at or beyond `bytes` read zero instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting on gfx9
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t clamp_bytes(size_t n) { return n < 0xffffffffu ? (uint32_t)n : 0xffffffffu; }
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);

@@ -21,6 +21,19 @@ typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
 constexpr int kWave = 64;
 constexpr float kE4M3Max = 448.0f;
 
+// ---------------------------------------------------------------- buffer access
+// Raw buffer access: a 128-bit descriptor in SGPRs (base, size in bytes) plus
+// a 32-bit lane offset and a scalar offset. Loads need no 64-bit VGPR address
+// arithmetic, and accesses at or beyond `bytes` read zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    // dword 3 = 0x00020000: 32-bit data format, the raw-buffer setting on gfx9
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t clamp_bytes(size_t n) { return n < 0xffffffffu ? (uint32_t)n : 0xffffffffu; }
+
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
