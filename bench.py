@@ -1,8 +1,9 @@
 """Benchmark of one DeepSeek-R1-style MoE layer on one MI355X.
 
-A step is one pass of the whole layer through the C ABI -- moe_route,
-moe_permute, moe_expert_ffn_gate_up, moe_expert_ffn_down, moe_combine -- over
-one batch of synthetic tokens already resident in HBM. The default workload
+A step is one pass of the whole layer through the C ABI -- moe_route (or,
+for batches of 4096 tokens and more, moe_route_select, which returns the same
+ids and weights), moe_permute, moe_expert_ffn_gate_up, moe_expert_ffn_down,
+moe_combine -- over one batch of synthetic tokens already resident in HBM. The default workload
 is the R1 decode layer in bf16: 256 tokens, hidden 7168, 256 routed experts
 (intermediate 2048, top-8 by sigmoid score with Zipf(1.1)-skewed popularity)
 plus one shared expert. Other workloads (--config 3, 4, 5) are available for

@@ -75,6 +75,28 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, moe
                      int T, int H, int E, int k, moe_scoring scoring, int renormalize,
                      float* logits, int32_t* topk_ids, float* topk_w, void* stream);
 
+/* Gating for large token batches: the same topk_ids and topk_w as moe_route
+ * (bit for bit), without computing every fixed-order logit. Approximate logits
+ * and sum_h |x_h w_eh| come from bf16 MFMAs; a rigorous bound on the distance
+ * between an approximate logit and the fixed-order one leaves, per token, the
+ * experts whose bound interval reaches the k-th largest lower bound. Only those
+ * get their fixed-order logit (the selection rule of moe_route is then applied
+ * to them, every other expert counting as -inf); the rest cannot be picked.
+ *   x [T,H], w_router [E,H] bf16; bias [E] fp32 or NULL; topk_ids [T,k] int32
+ *   (out), topk_w [T,k] fp32 (out); workspace: device memory of at least
+ *   moe_route_select_workspace_size(T, E) bytes, caller-owned, 256-byte
+ *   aligned; its contents on return are unspecified.
+ * Limits: bf16 only; H % 32 == 0 and H <= 8192; 1 <= k <= E <= 256; softmax
+ * scoring only with renormalize (the unrenormalised softmax needs every
+ * logit): MOE_ERR_UNSUPPORTED otherwise, MOE_ERR_WORKSPACE if ws_bytes is too
+ * small. Faster than moe_route for thousands of tokens; slower for a decode
+ * batch (the MFMA pass has one workgroup per 64 tokens). */
+size_t moe_route_select_workspace_size(int T, int E);
+moe_status moe_route_select(const void* x, const void* w_router, const float* bias, moe_dtype dt,
+                            int T, int H, int E, int k, moe_scoring scoring, int renormalize,
+                            int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                            void* stream);
+
 /* Token -> expert grouping ([Moreh-EP] Library optimization: the fused MoE
  * kernel consumes tokens grouped per expert; Inter-GPU load balancing: the
  * per-expert activation counts). Slots s = t*k + j whose id lies in

@@ -10,7 +10,8 @@ from ._lib import (BF16, F32, FP8_E4M3, SIGMOID, SOFTMAX, EXPORTS, MoEError, lib
                    moe_affinity_partition, moe_balanced_partition, moe_coactivation,
                    moe_combine, moe_count_accumulate, moe_expert_ffn, moe_expert_ffn_down,
                    moe_expert_ffn_gate_up, moe_expert_ffn_workspace_size, moe_gather_rows,
-                   moe_permute, moe_permute_workspace_size, moe_route)
+                   moe_permute, moe_permute_workspace_size, moe_route, moe_route_select,
+                   moe_route_select_workspace_size)
 from .layer import LayerBuffers, MoELayer
 
 

@@ -21,7 +21,7 @@ SOFTMAX, SIGMOID = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 EXPORTS = [
-    "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
+    "moe_route", "moe_route_select_workspace_size", "moe_route_select", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
     "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_balanced_partition", "moe_gather_rows",
     "moe_count_accumulate", "moe_coactivation", "moe_affinity_partition",
     "moe_status_string", "moe_last_error_message",
@@ -55,6 +55,9 @@ def lib() -> C.CDLL:
         L = C.CDLL(LIB_PATH)
         p, i, sz = C.c_void_p, C.c_int, C.c_size_t
         L.moe_route.argtypes = [p, p, p, i, i, i, i, i, i, i, p, p, p, p]
+        L.moe_route_select_workspace_size.argtypes = [i, i]
+        L.moe_route_select_workspace_size.restype = sz
+        L.moe_route_select.argtypes = [p, p, p, i, i, i, i, i, i, i, p, p, p, sz, p]
         L.moe_permute_workspace_size.argtypes = [i, i, i]
         L.moe_permute_workspace_size.restype = sz
         L.moe_permute.argtypes = [p, i, i, i, i, i, p, i, i, i, p, p, p, p, p, p, p, sz, p]
@@ -72,7 +75,7 @@ def lib() -> C.CDLL:
         L.moe_status_string.argtypes = [i]
         L.moe_status_string.restype = C.c_char_p
         L.moe_last_error_message.restype = C.c_char_p
-        for f in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_gate_up",
+        for f in ("moe_route", "moe_route_select", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_gate_up",
                   "moe_expert_ffn_down", "moe_combine",
                   "moe_balanced_partition", "moe_gather_rows", "moe_count_accumulate",
                   "moe_coactivation", "moe_affinity_partition"):
@@ -119,6 +122,17 @@ def moe_route(x, w_router, bias, dt, T, H, E, k, scoring, renormalize, logits, t
     _check("moe_route", lib().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), dt, T, H, E, k, scoring,
                                         int(bool(renormalize)), _ptr(logits), _ptr(topk_ids),
                                         _ptr(topk_w), _stream(stream)))
+
+
+def moe_route_select_workspace_size(T, E) -> int:
+    return int(lib().moe_route_select_workspace_size(T, E))
+
+
+def moe_route_select(x, w_router, bias, dt, T, H, E, k, scoring, renormalize, topk_ids, topk_w,
+                     workspace, ws_bytes, stream=None):
+    _check("moe_route_select", lib().moe_route_select(
+        _ptr(x), _ptr(w_router), _ptr(bias), dt, T, H, E, k, scoring, int(bool(renormalize)),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def moe_permute_workspace_size(T, k, E_local) -> int:

@@ -91,6 +91,36 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, moe
                         topk_ids, topk_w, (hipStream_t)stream);
 }
 
+size_t moe_route_select_workspace_size(int T, int E) {
+    if (T < 0 || E < 1) return 0;
+    return route_select_workspace_bytes(T, E);
+}
+
+moe_status moe_route_select(const void* x, const void* w_router, const float* bias, moe_dtype dt,
+                            int T, int H, int E, int k, moe_scoring scoring, int renormalize,
+                            int32_t* topk_ids, float* topk_w, void* workspace, size_t ws_bytes,
+                            void* stream) {
+    g_msg[0] = 0;
+    REQUIRE(T >= 0 && H >= 1 && E >= 1 && k >= 1, MOE_ERR_INVALID_ARG,
+            "moe_route_select: need T >= 0, H >= 1, E >= 1, k >= 1 (T=%d H=%d E=%d k=%d)", T, H, E, k);
+    REQUIRE(k <= E, MOE_ERR_INVALID_ARG, "moe_route_select: k=%d > E=%d", k, E);
+    REQUIRE(scoring == MOE_SOFTMAX || scoring == MOE_SIGMOID, MOE_ERR_INVALID_ARG,
+            "moe_route_select: unknown scoring %d", (int)scoring);
+    REQUIRE(E <= 256, MOE_ERR_UNSUPPORTED, "moe_route_select: E=%d > 256", E);
+    REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_route_select: dt must be MOE_BF16");
+    REQUIRE(H % 32 == 0 && H <= 8192, MOE_ERR_UNSUPPORTED,
+            "moe_route_select: need H %% 32 == 0 and H <= 8192 (H=%d)", H);
+    REQUIRE(scoring == MOE_SIGMOID || renormalize, MOE_ERR_UNSUPPORTED,
+            "moe_route_select: softmax without renormalisation needs every logit (use moe_route)");
+    if (T == 0) return MOE_OK;
+    REQUIRE(x && w_router && topk_ids && topk_w, MOE_ERR_INVALID_ARG, "moe_route_select: null pointer");
+    const size_t need = route_select_workspace_bytes(T, E);
+    REQUIRE(workspace && ws_bytes >= need, MOE_ERR_WORKSPACE,
+            "moe_route_select: workspace %zu < %zu bytes", ws_bytes, need);
+    return launch_route_select(x, w_router, bias, T, H, E, k, scoring, renormalize ? 1 : 0, topk_ids,
+                               topk_w, workspace, (hipStream_t)stream);
+}
+
 size_t moe_permute_workspace_size(int T, int k, int E_local) {
     if (T < 0 || k < 1 || E_local < 1) return 0;
     return permute_workspace_bytes(T, k, E_local);

@@ -79,6 +79,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 moe_status launch_route(const void* x, const void* w, const float* bias, moe_dtype dt, int T, int H,
                         int E, int k, int scoring, int renorm, float* logits, int32_t* ids,
                         float* topk_w, hipStream_t st);
+size_t route_select_workspace_bytes(int T, int E);
+moe_status launch_route_select(const void* x, const void* w, const float* bias, int T, int H, int E,
+                               int k, int scoring, int renorm, int32_t* ids, float* topk_w, void* ws,
+                               hipStream_t st);
 
 size_t permute_workspace_bytes(int T, int k, int E_local);
 moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_local, int include_shared,

@@ -33,6 +33,7 @@ class LayerBuffers:
     out: torch.Tensor
     ws_perm: torch.Tensor
     ws_ffn: torch.Tensor
+    ws_route: Optional[torch.Tensor] = None  # moe_route_select's workspace (large batches)
 
 
 class MoELayer:
@@ -62,6 +63,20 @@ class MoELayer:
                                       sh.get("w2_scale"))
         self.n_groups = self.E_local + (1 if shared is not None else 0)
         self._bufs = {}
+
+    # Batches of at least this many tokens route through moe_route_select
+    # (same ids and weights as moe_route; faster once the MFMA pass has a few
+    # thousand tokens, slower for a decode batch). The logits buffer is then
+    # left unfilled.
+    ROUTE_SELECT_MIN_T = 4096
+
+    def uses_route_select(self, T: int) -> bool:
+        r = self.router
+        if r is None or self.act_dt != L.BF16 or T < self.ROUTE_SELECT_MIN_T:
+            return False
+        E = r["w"].shape[0]
+        return (self.H % 32 == 0 and self.H <= 8192 and E <= 256
+                and (r["scoring"] == L.SIGMOID or r.get("renormalize", True)))
 
     # ------------------------------------------------------------------ buffers
     def buffers(self, T: int, device=None) -> LayerBuffers:
@@ -93,6 +108,9 @@ class MoELayer:
             ws_perm=torch.empty(max(ws_p, 1), dtype=torch.uint8, device=device),
             ws_ffn=torch.empty(max(ws_f, 1), dtype=torch.uint8, device=device),
         )
+        if self.uses_route_select(T):
+            b.ws_route = torch.empty(L.moe_route_select_workspace_size(T, E), dtype=torch.uint8,
+                                     device=device)
         self._bufs[T] = b
         return b
 
@@ -101,8 +119,13 @@ class MoELayer:
         r = self.router
         T, H = x.shape
         E = r["w"].shape[0]
-        L.moe_route(x, r["w"], r.get("bias"), self.act_dt, T, H, E, self.k, r["scoring"],
-                    r.get("renormalize", True), b.logits, b.topk_ids, b.topk_w, stream)
+        if b.ws_route is not None:
+            L.moe_route_select(x, r["w"], r.get("bias"), self.act_dt, T, H, E, self.k, r["scoring"],
+                               r.get("renormalize", True), b.topk_ids, b.topk_w, b.ws_route,
+                               b.ws_route.numel(), stream)
+        else:
+            L.moe_route(x, r["w"], r.get("bias"), self.act_dt, T, H, E, self.k, r["scoring"],
+                        r.get("renormalize", True), b.logits, b.topk_ids, b.topk_w, stream)
 
     def permute(self, x: torch.Tensor, b: LayerBuffers, topk_ids=None, stream=None):
         T = x.shape[0]

@@ -57,7 +57,8 @@ def _full_check(cfg, layer, b, x, st, sh, n_sample, seed=0):
     lg, ids, w = oracle.route(x.cpu(), layer.router["w"].cpu(),
                               None if layer.router["bias"] is None else layer.router["bias"].cpu(),
                               cfg.k, oracle.SIGMOID, True)
-    assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), lg.view(np.uint32))
+    if not layer.uses_route_select(T):  # moe_route_select leaves the logits buffer unfilled
+        assert np.array_equal(b.logits.cpu().numpy().view(np.uint32), lg.view(np.uint32))
     assert np.array_equal(b.topk_ids.cpu().numpy(), ids)
     assert np.abs(b.topk_w.cpu().numpy() - w).max() <= 1e-6
     p = oracle.permute(ids, cfg.expert_base, layer.E_local, sh is not None)
