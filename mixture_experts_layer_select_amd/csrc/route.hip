@@ -272,7 +272,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 //   2. route_refine_kernel, one wave per token: every bound below is taken in
 //      fp64 with a margin. Whatever the MFMA's internal summation order, with
 //      fp32-or-better intermediates and at most 2 units of fp32 rounding per
-//      step (u = 2^-22: twice truncation), |a_e - S_e| <= g(H) s_e/(1 - g(H))
+//      step (u = 2^-22: twice truncation), |a_e - S_e| <= g(n) s_e/(1 - g(n))
+//      with n = H + 64 additions (the K tail of the last stage is zeros)
 //      (S_e the exact dot product, g(n) = n u/(1 - n u)), plus H * 2^-126 for
 //      flushed tiny products. The fixed-order value c_e differs from S_e by at
 //      most g'(8 ceil(H/512) + 6) s_e (round to nearest, 2^-24: each lane's
@@ -284,37 +285,97 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 //      remaining candidates (at least k) get their fixed-order logit, the rest
 //      -inf, written over the approximations.
 //   3. route_topk_kernel as in moe_route: ids and weights are those of moe_route.
-constexpr int kApproxT = 32;   // tokens per workgroup
-constexpr int kApproxE = 64;   // experts per wave (4 waves: 256 experts)
-constexpr int kApproxK = 32;   // K per MFMA
+constexpr int kApproxT = 128;  // tokens per workgroup
+constexpr int kApproxE = 128;  // experts per workgroup
+constexpr int kApproxK = 64;   // K per stage
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                      __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// H % 32 == 0; blockIdx.x: 32-token block; wave w: experts 64w + [0, 64).
-// A operand = 16 expert rows, B = 16 token rows; lane (li, lk) supplies
-// k = 32c + 8lk + [0, 8) of row li, and holds D[4lk + r][li] (expert 4lk + r
-// of the block, token li). Operands of K steps c+1 and c+2 are in flight
-// while step c computes (a 3-slot ring). Rows past T or E read a valid row;
-// never stored.
-__global__ __launch_bounds__(256) void route_approx_kernel(const uint16_t* __restrict__ x,
+// this wave's LDS accesses done (lgkmcnt 0), then a workgroup barrier without
+// the release fence of __syncthreads(), which would also wait for every load
+// in flight (the register ring)
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+}
+
+struct ApproxStage {
+    uint16_t x[kApproxT * kApproxK];  // 16 KB: 128 rows of 128 bytes
+    uint16_t w[kApproxE * kApproxK];  // 16 KB
+};
+
+// Tile of 128 tokens x 128 experts, 8 waves: wave (wt, we) = tokens 32wt +
+// [0, 32), experts 64we + [0, 64). Each K stage (64) of both operand tiles is
+// loaded by all 512 threads into registers one stage ahead, then stored to
+// one of two LDS buffers; rows are 128 bytes and chunk c (16 bytes) of row r
+// sits at physical chunk c ^ ((r >> 1) & 7). A operand = 16 expert rows, B =
+// 16 token rows; lane (li, lk) supplies k = 32 sub + 8 lk + [0, 8) of row li
+// and holds D[4lk + r][li] (expert 4lk + r of the block, token li). Rows past
+// T or E read a valid row and columns past H read zeros (their products add
+// exact zeros); neither is stored.
+__global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w, int T,
                                                            int H, int E, float* __restrict__ approx,
                                                            float* __restrict__ sabs) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(1024))) ApproxStage st[2];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wt = wave & 3, we = wave >> 2;
     const int li = lane & 15, lk = lane >> 4;
     const int t0 = blockIdx.x * kApproxT;
-    const int e0 = wave * kApproxE;
-    if (e0 >= E) return;
-    const uint16_t* xr[2];
-    const uint16_t* wr[4];
+    const int e0 = blockIdx.y * kApproxE;
+    const int nst = (H + kApproxK - 1) / kApproxK;
+
+    // this thread's 2 + 2 chunks of a stage: chunk q = tid + 512 i -> row q / 8,
+    // chunk q % 8; a 3-slot register ring holds stages s+1 and s+2 (in flight)
+    // while stage s is computed from LDS
+    u32x4 rx[3][2], rw[3][2];
+    // rows through descriptors of the tile's rows: columns past H read zeros
+    const int xrows = min(kApproxT, T - t0), wrows = min(kApproxE, E - e0);
+    const __amdgpu_buffer_rsrc_t xd = buffer_rsrc(x + (size_t)t0 * H, (uint32_t)((size_t)xrows * H * 2));
+    const __amdgpu_buffer_rsrc_t wd = buffer_rsrc(w + (size_t)e0 * H, (uint32_t)((size_t)wrows * H * 2));
+    uint32_t xo[2], wo[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) xr[b] = x + (size_t)min(t0 + 16 * b + li, T - 1) * H + 8 * lk;
+    for (int i = 0; i < 2; ++i) {
+        const int q = tid + 512 * i;
+        const int r = q >> 3, c = q & 7;
+        xo[i] = (uint32_t)(min(r, xrows - 1) * H + 8 * c) * 2u;
+        wo[i] = (uint32_t)(min(r, wrows - 1) * H + 8 * c) * 2u;
+    }
+    auto load = [&](int slot, int sidx) {
+        const int k0 = min(sidx, nst - 1) * kApproxK;  // past the end: a reload, never stored
+        // a chunk past H (only in a last stage of 32 columns) is masked out
+        // by zeroing its value below, never by a branch around the load
 #pragma unroll
-    for (int b = 0; b < 4; ++b) wr[b] = w + (size_t)min(e0 + 16 * b + li, E - 1) * H + 8 * lk;
+        for (int i = 0; i < 2; ++i) {
+            rx[slot][i] = buffer_load16(xd, xo[i], (uint32_t)k0 * 2u);
+            rw[slot][i] = buffer_load16(wd, wo[i], (uint32_t)k0 * 2u);
+        }
+        if (k0 + kApproxK > H) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c = (tid + 512 * i) & 7;
+                if (k0 + 8 * c >= H) {
+                    rx[slot][i] = u32x4{0u, 0u, 0u, 0u};
+                    rw[slot][i] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+    };
+    auto store = [&](int slot, ApproxStage& S) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 512 * i;
+            const int r = q >> 3, c = q & 7;
+            const int o = r * kApproxK + ((c ^ ((r >> 1) & 7)) << 3);
+            *reinterpret_cast<u32x4*>(&S.x[o]) = rx[slot][i];
+            *reinterpret_cast<u32x4*>(&S.w[o]) = rw[slot][i];
+        }
+    };
     f32x4 acc[4][2], aab[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -323,56 +384,69 @@ __global__ __launch_bounds__(256) void route_approx_kernel(const uint16_t* __res
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             aab[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    const int nk = H / kApproxK;
-    u32x4 fa[3][4], fb[3][2];
-    auto load = [&](int slot, int c) {
-        const int k0 = (c < nk ? c : nk - 1) * kApproxK;  // past the end: a reload, never used
-#pragma unroll
-        for (int b = 0; b < 4; ++b) fa[slot][b] = *reinterpret_cast<const u32x4*>(wr[b] + k0);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) fb[slot][b] = *reinterpret_cast<const u32x4*>(xr[b] + k0);
+    auto frag = [&](const uint16_t* base, int row, int sub) {
+        const int c = 4 * sub + lk;
+        return *reinterpret_cast<const u32x4*>(&base[row * kApproxK + ((c ^ ((row >> 1) & 7)) << 3)]);
     };
-    auto step = [&](int slot) {
-        u32x4 ga[4], gb[2];
+    auto compute = [&](const ApproxStage& S) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) ga[b] = fa[slot][b] & 0x7fff7fffu;  // |bf16| pairs
+        for (int sub = 0; sub < 2; ++sub) {
+            u32x4 fa[4], fb[2], ga[4], gb[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) gb[b] = fb[slot][b] & 0x7fff7fffu;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                acc[i][j] = mfma16x16x32(fa[slot][i], fb[slot][j], acc[i][j]);
-                aab[i][j] = mfma16x16x32(ga[i], gb[j], aab[i][j]);
+            for (int b = 0; b < 4; ++b) {
+                fa[b] = frag(S.w, 64 * we + 16 * b + li, sub);
+                ga[b] = fa[b] & 0x7fff7fffu;  // |bf16| pairs: sign bits cleared
             }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                fb[b] = frag(S.x, 32 * wt + 16 * b + li, sub);
+                gb[b] = fb[b] & 0x7fff7fffu;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+                    aab[i][j] = mfma16x16x32(ga[i], gb[j], aab[i][j]);
+                }
+        }
     };
-    // the scheduling barriers keep each step's loads ahead of the previous
-    // step's MFMAs (the compiler would otherwise sink them next to their use)
+    // step s (u = s mod 6 fixes the register slot and the LDS buffer):
+    // compute stage s from LDS buffer s%2, store stage s+1 from its register
+    // slot into the other buffer (read two steps ago), meet, then load stage
+    // s+3 into the slot stage s came from. The loop leaves from the middle.
     load(0, 0);
     load(1, 1);
-    for (int c = 0;; c += 3) {
-        load(2, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        step(0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 >= nk) break;
-        load(0, c + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        step(1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 2 >= nk) break;
-        load(1, c + 4);
-        __builtin_amdgcn_sched_barrier(0);
-        step(2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 3 >= nk) break;
+    load(2, 2);
+    store(0, st[0]);
+    lds_barrier();
+    auto step = [&](int sidx, auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        compute(st[u & 1]);
+        if (sidx + 1 < nst) store((u + 1) % 3, st[(u + 1) & 1]);
+        lds_barrier();
+        load(u % 3, sidx + 3);
+    };
+    for (int sidx = 0;; sidx += 6) {
+        step(sidx, std::integral_constant<int, 0>{});
+        if (sidx + 1 >= nst) break;
+        step(sidx + 1, std::integral_constant<int, 1>{});
+        if (sidx + 2 >= nst) break;
+        step(sidx + 2, std::integral_constant<int, 2>{});
+        if (sidx + 3 >= nst) break;
+        step(sidx + 3, std::integral_constant<int, 3>{});
+        if (sidx + 4 >= nst) break;
+        step(sidx + 4, std::integral_constant<int, 4>{});
+        if (sidx + 5 >= nst) break;
+        step(sidx + 5, std::integral_constant<int, 5>{});
+        if (sidx + 6 >= nst) break;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int t = t0 + 16 * j + li;
-            const int e = e0 + 16 * i + 4 * lk;
+            const int t = t0 + 32 * wt + 16 * j + li;
+            const int e = e0 + 64 * we + 16 * i + 4 * lk;
             if (t < T) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -386,20 +460,20 @@ __global__ __launch_bounds__(256) void route_approx_kernel(const uint16_t* __res
 
 __device__ __forceinline__ double gamma_n(double n, double u) { return n * u / (1.0 - n * u); }
 
-// one wave per token; E <= 256, H % 32 == 0, H <= 16 * 512 (the token's row
-// stays in 16 registers per lane)
+// one wave per token; E <= 256, H % 32 == 0, H <= kMaxSteps * 512 (the
+// token's row stays in registers: kMaxSteps chunks per lane)
+template <int kMaxSteps>
 __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w,
                                                            const float* __restrict__ bias, int T,
                                                            int H, int E, int k,
                                                            float* __restrict__ logits,
                                                            const float* __restrict__ sabs) {
-    constexpr int kMaxSteps = 16;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const int nsteps = (H + 511) / 512;
-    const double gm = gamma_n((double)H, 0x1p-22);
+    const int nsteps = (H + 511) / 512;  // steps with data; the rest read zeros
+    const double gm = gamma_n((double)H + 64.0, 0x1p-22);  // zero-padded K tail included
     const double gc = gamma_n(8.0 * nsteps + 6.0, 0x1p-24);
     // bounds of every expert's logit, rounded outward to fp32
     float lo[4], hi[4];
@@ -439,60 +513,64 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __res
         kth = best;
     }
     const float L = from_ordered((uint32_t)(kth >> 32));
-    // this token's row of x, one 8-element chunk per lane and step
-    const uint16_t* xrow = x + (size_t)t * H;
+    // this token's row of x, one 8-element chunk per lane and step. Rows are
+    // read through a descriptor of the row's size: chunks past H read zeros,
+    // whose products add exact zeros to a partial (which is never -0), so all
+    // kMaxSteps steps run unguarded and every load can be issued up front
+    const __amdgpu_buffer_rsrc_t xd = buffer_rsrc(x + (size_t)t * H, (uint32_t)H * 2u);
     u32x4 xc[kMaxSteps];
 #pragma unroll
-    for (int s = 0; s < kMaxSteps; ++s)
-        if (s < nsteps) {
-            const int h0 = 512 * s + 8 * lane;
-            xc[s] = h0 < H ? *reinterpret_cast<const u32x4*>(xrow + h0) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int s = 0; s < kMaxSteps; ++s) xc[s] = buffer_load16(xd, (uint32_t)(512 * s + 8 * lane) * 2u, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e_lane = lane + 64 * i;
         uint64_t cand = __ballot(e_lane < E && hi[i] >= L);
         float mine = -__builtin_inff();
-        // candidates two at a time: two independent multiply-add chains
-        while (cand) {
-            const int c0 = __builtin_ctzll(cand);
-            cand &= cand - 1;
-            const bool two = cand != 0;
-            const int c1 = two ? __builtin_ctzll(cand) : c0;
-            if (two) cand &= cand - 1;
-            // fixed-order logit: lane j sums its chunks in ascending h with
-            // fused multiply-adds from +0, then p[j] += p[j + s], s = 32..1
-            const uint16_t* w0 = w + (size_t)(64 * i + c0) * H;
-            const uint16_t* w1 = w + (size_t)(64 * i + c1) * H;
-            float p0 = 0.0f, p1 = 0.0f;
+        // one candidate at a time; the next candidate's row is loaded while
+        // the current one is summed (after the last, the same row again, so
+        // every step issues the same number of loads)
+        auto load_row = [&](int c, u32x4* r) {
+            const __amdgpu_buffer_rsrc_t d = buffer_rsrc(w + (size_t)(64 * i + c) * H, (uint32_t)H * 2u);
+#pragma unroll
+            for (int s = 0; s < kMaxSteps; ++s) r[s] = buffer_load16(d, (uint32_t)(512 * s + 8 * lane) * 2u, 0);
+        };
+        // fixed-order logit: lane j sums its chunks in ascending h with
+        // fused multiply-adds from +0, then p[j] += p[j + s], s = 32..1
+        auto logit = [&](int c, const u32x4* r) {
+            float p = 0.0f;
 #pragma unroll
             for (int s = 0; s < kMaxSteps; ++s)
-                if (s < nsteps) {
-                    const int h0 = 512 * s + 8 * lane;
-                    if (h0 < H) {
-                        const u32x4 a0 = *reinterpret_cast<const u32x4*>(w0 + h0);
-                        const u32x4 a1 = *reinterpret_cast<const u32x4*>(w1 + h0);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            p0 = __builtin_fmaf(bf16_lo(xc[s][q]), bf16_lo(a0[q]), p0);
-                            p1 = __builtin_fmaf(bf16_lo(xc[s][q]), bf16_lo(a1[q]), p1);
-                            p0 = __builtin_fmaf(bf16_hi(xc[s][q]), bf16_hi(a0[q]), p0);
-                            p1 = __builtin_fmaf(bf16_hi(xc[s][q]), bf16_hi(a1[q]), p1);
-                        }
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    p = __builtin_fmaf(bf16_lo(xc[s][q]), bf16_lo(r[s][q]), p);
+                    p = __builtin_fmaf(bf16_hi(xc[s][q]), bf16_hi(r[s][q]), p);
                 }
 #pragma unroll
-            for (int s = 32; s >= 1; s >>= 1) {
-                p0 = p0 + __shfl_xor(p0, s);
-                p1 = p1 + __shfl_xor(p1, s);
+            for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s);
+            float l = __shfl(p, 0);
+            if (bias) l = l + bias[64 * i + c];
+            if (lane == c) mine = l;
+        };
+        if (cand) {
+            u32x4 ra[kMaxSteps], rb[kMaxSteps];
+            int ca = __builtin_ctzll(cand);
+            cand &= cand - 1;
+            load_row(ca, ra);
+            for (;;) {
+                const bool hb = cand != 0;
+                const int cb = hb ? __builtin_ctzll(cand) : ca;
+                if (hb) cand &= cand - 1;
+                load_row(cb, rb);
+                logit(ca, ra);
+                if (!hb) break;
+                const bool ha = cand != 0;
+                const int cn = ha ? __builtin_ctzll(cand) : cb;
+                if (ha) cand &= cand - 1;
+                load_row(cn, ra);
+                logit(cb, rb);
+                if (!ha) break;
+                ca = cn;
             }
-            float l0 = __shfl(p0, 0), l1 = __shfl(p1, 0);
-            if (bias) {
-                l0 = l0 + bias[64 * i + c0];
-                l1 = l1 + bias[64 * i + c1];
-            }
-            if (lane == c0) mine = l0;
-            if (two && lane == c1) mine = l1;
         }
         if (e_lane < E) logits[(size_t)t * E + e_lane] = mine;
     }
@@ -530,11 +608,17 @@ moe_status launch_route_select(const void* x, const void* w, const float* bias, 
                                hipStream_t st) {
     float* approx = (float*)ws;
     float* sabs = (float*)((uint8_t*)ws + align_up((size_t)T * E * sizeof(float), 256));
-    hipLaunchKernelGGL(route_approx_kernel, dim3((T + kApproxT - 1) / kApproxT), dim3(256), 0, st,
+    hipLaunchKernelGGL(route_approx_kernel,
+                       dim3((T + kApproxT - 1) / kApproxT, (E + kApproxE - 1) / kApproxE), dim3(512), 0, st,
                        (const uint16_t*)x, (const uint16_t*)w, T, H, E, approx, sabs);
     moe_status s = check_launch("route_approx_kernel");
     if (s != MOE_OK) return s;
-    hipLaunchKernelGGL(route_refine_kernel, dim3((T + 3) / 4), dim3(256), 0, st, (const uint16_t*)x,
+    // the smallest register-resident row that holds H (H <= 8192)
+    const int nsteps = (H + 511) / 512;
+    auto refine = nsteps <= 4 ? route_refine_kernel<4>
+                : nsteps <= 8 ? route_refine_kernel<8>
+                : nsteps <= 14 ? route_refine_kernel<14> : route_refine_kernel<16>;
+    hipLaunchKernelGGL(refine, dim3((T + 3) / 4), dim3(256), 0, st, (const uint16_t*)x,
                        (const uint16_t*)w, bias, T, H, E, k, approx, sabs);
     s = check_launch("route_refine_kernel");
     if (s != MOE_OK) return s;
