@@ -114,6 +114,7 @@ moe_status moe_route_select(const void* x, const void* w_router, const float* bi
  *   b*(T*k+T) + r): per 1x128 block s = amax/448 (1 for
  *   an all-zero block), code = e4m3(clamp(v/s, +-448)), fp32 division, round to
  *   nearest even. x and x_perm may both be NULL (maps and counts only).
+ *   Rows of x_perm past the used ones are unspecified.
  * ids outside the local range (including negative ones) are simply not local.
  * Limits: 1 <= E_local <= 256; T*k+T < 2^31; fp8 needs H % 128 == 0.
  * workspace: moe_permute_workspace_size(T, k, E_local) bytes. */

@@ -251,55 +251,129 @@ __global__ __launch_bounds__(256) void perm_gather_copy_kernel(
 }
 
 // bf16 rows -> e4m3 codes + one fp32 scale per 128 elements; H % 128 == 0.
-// 16 lanes own one 128-element block, 8 elements each. Scales are K-major:
-// block b of row r at b * cap + r.
+// 16 lanes own one 128-element block, 8 elements each; a pass of four rounds
+// issues all of its row loads before the first block is quantised. Scales are
+// K-major: block b of row r at b * cap + r.
+__device__ __forceinline__ void quant_row_fp8(const uint16_t* __restrict__ src, int H, long cap,
+                                              long r, uint8_t* __restrict__ x_perm,
+                                              float* __restrict__ x_scale) {
+    const int nb = H / 128;
+    const int sub = threadIdx.x & 15;
+    for (int b0 = threadIdx.x >> 4; b0 < nb; b0 += 64) {
+        u32x4 q[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = b0 + 16 * i;
+            if (b < nb) q[i] = *reinterpret_cast<const u32x4*>(src + b * 128 + sub * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = b0 + 16 * i;
+            if (b >= nb) break;
+            const int h0 = b * 128 + sub * 8;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = bf16_lo(q[i][e]);
+                v[2 * e + 1] = bf16_hi(q[i][e]);
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
+            const float sc = block_scale(a);
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = clamp_e4m3(v[e] / sc);
+            const uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
+            const uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
+            *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
+            if (sub == 0) x_scale[b * cap + r] = sc;
+        }
+    }
+}
+
+// one pass: every used row quantises its token's row (the next row's token
+// index is loaded before this row's work)
 __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ row_to_slot,
     const int32_t* __restrict__ offsets, int E_local, long S, int k, int H, long cap,
     uint8_t* __restrict__ x_perm, float* __restrict__ x_scale) {
     const long used = offsets[E_local + 1];
-    const int nb = H / 128;
-    const int sub = threadIdx.x & 15;
-    // 16 threads per 128-column block, 16 blocks per pass; a pass of four
-    // rounds issues all of its row loads before the first block is quantised,
-    // and the next row's token index is loaded before this row's work
     long r = blockIdx.x;
     int32_t slot = r < used ? row_to_slot[r] : 0;
     for (; r < used; r += gridDim.x) {
         const long t = token_of(slot, S, k);
         if (r + gridDim.x < used) slot = row_to_slot[r + gridDim.x];
-        const uint16_t* src = x + t * H;
-        for (int b0 = threadIdx.x >> 4; b0 < nb; b0 += 64) {
-            u32x4 q[4];
+        quant_row_fp8(x + t * H, H, cap, r, x_perm, x_scale);
+    }
+}
+
+// Two passes (with a shared group): each token is quantised once into the
+// shared group's rows [R, R + T), which hold the tokens in order anyway, and
+// the routed rows copy their token's codes and scales from there. Without a
+// shared group the staging rows would be [T*k, T*k + T), which no routed row
+// reaches (R <= T*k).
+__device__ __forceinline__ long stage_row0(const int32_t* __restrict__ offsets, int E_local, long S) {
+    const long R = offsets[E_local];
+    return offsets[E_local + 1] > R ? R : S;
+}
+
+// pass 1: every token quantised once, into its staging row
+__global__ __launch_bounds__(256) void perm_quant_tokens_fp8_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets, int E_local, long S, int T,
+    int H, long cap, uint8_t* __restrict__ x_perm, float* __restrict__ x_scale) {
+    const long q0 = stage_row0(offsets, E_local, S);
+    for (long t = blockIdx.x; t < T; t += gridDim.x)
+        quant_row_fp8(x + t * H, H, cap, q0 + t, x_perm, x_scale);
+}
+
+// pass 2: routed row r takes the codes and scales of its token's staging row.
+// A workgroup copies 16 consecutive rows: their tokens go to LDS once, the
+// codes move as 16-byte chunks over all (row, chunk) pairs, eight loads in
+// flight per thread, and each scale block is written for 16 consecutive rows
+// at once.
+constexpr int kCopyRows = 16;
+__global__ __launch_bounds__(256) void perm_copy_fp8_kernel(
+    const int32_t* __restrict__ row_to_slot, const int32_t* __restrict__ offsets, int E_local,
+    long S, int k, int H, long cap, uint8_t* __restrict__ x_perm, float* __restrict__ x_scale) {
+    __shared__ long tok[kCopyRows];
+    const long R = offsets[E_local];
+    const long q0 = stage_row0(offsets, E_local, S);
+    const int nb = H / 128;
+    const int nc = H / 16;
+    for (long r0 = (long)blockIdx.x * kCopyRows; r0 < R; r0 += (long)gridDim.x * kCopyRows) {
+        const int n = (int)min((long)kCopyRows, R - r0);
+        __syncthreads();
+        if (threadIdx.x < n) tok[threadIdx.x] = token_of(row_to_slot[r0 + threadIdx.x], S, k);
+        __syncthreads();
+        {
+            const int j = threadIdx.x & (kCopyRows - 1);
+            if (j < n) {
+                const long src = q0 + tok[j];
+                for (int b = threadIdx.x / kCopyRows; b < nb; b += 256 / kCopyRows)
+                    x_scale[b * cap + r0 + j] = x_scale[b * cap + src];
+            }
+        }
+        const int total = n * nc;
+        for (int i0 = threadIdx.x; i0 < total; i0 += 8 * 256) {
+            u32x4 v[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int b = b0 + 16 * i;
-                if (b < nb) q[i] = *reinterpret_cast<const u32x4*>(src + b * 128 + sub * 8);
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u;
+                if (i < total) {
+                    const int rr = i / nc, c = i - rr * nc;
+                    v[u] = *reinterpret_cast<const u32x4*>(x_perm + (q0 + tok[rr]) * H + 16 * c);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int b = b0 + 16 * i;
-                if (b >= nb) break;
-                const int h0 = b * 128 + sub * 8;
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[2 * e] = bf16_lo(q[i][e]);
-                    v[2 * e + 1] = bf16_hi(q[i][e]);
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + 256 * u;
+                if (i < total) {
+                    const int rr = i / nc, c = i - rr * nc;
+                    *reinterpret_cast<u32x4*>(x_perm + (r0 + rr) * H + 16 * c) = v[u];
                 }
-                float a = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
-#pragma unroll
-                for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
-                const float sc = block_scale(a);
-                float qv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = clamp_e4m3(v[e] / sc);
-                const uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
-                const uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
-                *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
-                if (sub == 0) x_scale[b * cap + r] = sc;
             }
         }
     }
@@ -309,8 +383,8 @@ __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
 
 static moe_status launch_gather(const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt,
                                 const int32_t* row_to_slot, const int32_t* offsets, int E_local,
-                                long S, int k, long cap, void* x_perm, float* x_perm_scale,
-                                hipStream_t st);
+                                long S, int k, long cap, int include_shared, void* x_perm,
+                                float* x_perm_scale, hipStream_t st);
 
 size_t permute_workspace_bytes(int T, int k, int E_local) {
     long S = (long)T * k;
@@ -341,7 +415,7 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_loca
                            slot_to_row);
         if ((s = check_launch("perm_small_kernel"))) return s;
         return launch_gather(x, x_dt, H, perm_dt, row_to_slot, offsets, E_local, S, k, cap,
-                             x_perm, x_perm_scale, st);
+                             include_shared, x_perm, x_perm_scale, st);
     }
     hipLaunchKernelGGL(perm_hist_kernel, dim3(n_chunks), dim3(256), 0, st, ids, S, base, E_local,
                        chunk_counts);
@@ -356,22 +430,36 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_loca
     hipLaunchKernelGGL(perm_fill_kernel, dim3(fill_blocks), dim3(256), 0, st, offsets, E_local, S, cap,
                        row_to_slot);
     if ((s = check_launch("perm_fill_kernel"))) return s;
-    return launch_gather(x, x_dt, H, perm_dt, row_to_slot, offsets, E_local, S, k, cap, x_perm,
-                         x_perm_scale, st);
+    return launch_gather(x, x_dt, H, perm_dt, row_to_slot, offsets, E_local, S, k, cap,
+                         include_shared, x_perm, x_perm_scale, st);
 }
 
 static moe_status launch_gather(const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt,
                                 const int32_t* row_to_slot, const int32_t* offsets, int E_local,
-                                long S, int k, long cap, void* x_perm, float* x_perm_scale,
-                                hipStream_t st) {
+                                long S, int k, long cap, int include_shared, void* x_perm,
+                                float* x_perm_scale, hipStream_t st) {
     if (!x_perm) return MOE_OK;
     const int cu = device_info().cu_count;
     const int gather_blocks = (int)std::min<long>(cap, (long)cu * 8);
-    if (perm_dt == MOE_FP8_E4M3) {
+    if (perm_dt == MOE_FP8_E4M3 && !include_shared) {
         hipLaunchKernelGGL(perm_gather_fp8_kernel, dim3(gather_blocks), dim3(256), 0, st,
                            (const uint16_t*)x, row_to_slot, offsets, E_local, S, k, H, cap,
                            (uint8_t*)x_perm, x_perm_scale);
         return check_launch("perm_gather_fp8_kernel");
+    }
+    if (perm_dt == MOE_FP8_E4M3) {
+        // with the shared group: each token is quantised once (into its shared
+        // row), then routed rows copy their token's codes and scales
+        const int T = (int)(cap - S);
+        hipLaunchKernelGGL(perm_quant_tokens_fp8_kernel, dim3((int)std::min<long>(T, (long)cu * 8)),
+                           dim3(256), 0, st, (const uint16_t*)x, offsets, E_local, S, T, H, cap,
+                           (uint8_t*)x_perm, x_perm_scale);
+        moe_status s = check_launch("perm_quant_tokens_fp8_kernel");
+        if (s != MOE_OK) return s;
+        const int copy_blocks = (int)std::max<long>(1, std::min<long>((S + kCopyRows - 1) / kCopyRows, (long)cu * 8));
+        hipLaunchKernelGGL(perm_copy_fp8_kernel, dim3(copy_blocks), dim3(256), 0, st, row_to_slot, offsets,
+                           E_local, S, k, H, cap, (uint8_t*)x_perm, x_perm_scale);
+        return check_launch("perm_copy_fp8_kernel");
     }
     const long eb = x_dt == MOE_F32 ? 4 : 2;
     hipLaunchKernelGGL(perm_gather_copy_kernel, dim3(gather_blocks), dim3(256), 0, st,
