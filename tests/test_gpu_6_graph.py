@@ -13,11 +13,12 @@ from gpu_util import DEV, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-def test_layer_graph_replays_match_eager(fmt):
+@pytest.mark.parametrize("fmt,T", [("bf16", 48), ("fp8", 48), ("bf16", 4096)])
+def test_layer_graph_replays_match_eager(fmt, T):
+    # T = 4096 routes through moe_route_select (the layer's large-batch gating)
     import mixture_experts_layer_select_amd as L
     base = mi.CONFIGS[2] if fmt == "bf16" else mi.CONFIGS[4]
-    cfg = mi.scaled(base, T=48, H=512, E=24, I=256, k=4, cid=160)
+    cfg = mi.scaled(base, T=T, H=512, E=24, I=256, k=4, cid=160)
     say(f"graph replay {fmt} T={cfg.T} H={cfg.H} E={cfg.E} I={cfg.I} k={cfg.k}")
     st = mi.stacked_expert_weights(cfg, range(cfg.E), device=DEV)
     sh = mi.shared_weights(cfg, device=DEV)
@@ -28,6 +29,7 @@ def test_layer_graph_replays_match_eager(fmt):
     x = mi.tokens(cfg, device=DEV)
     batches = [mi.normal(tuple(x.shape), cfg.x_std, 9100 + i, DEV, x.dtype) for i in range(3)]
 
+    assert layer.uses_route_select(T) == (T >= layer.ROUTE_SELECT_MIN_T)
     layer.forward(x)  # eager warm-up: buffers and one-time library set-up outside capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
