@@ -49,12 +49,22 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
     __shared__ int tot[kMaxLocal + 1];
     __shared__ int excl[kMaxLocal + 2];
     const int e = threadIdx.x;
+    // each thread walks its expert's column of chunk counts in batches of 16
+    // independent loads (one memory latency per batch, not per chunk)
+    constexpr int kB = 16;
     if (e < E_local) {
         int run = 0;
-        for (int c = 0; c < n_chunks; ++c) {
-            int v = chunk_counts[(size_t)c * E_local + e];
-            chunk_counts[(size_t)c * E_local + e] = run;
-            run += v;
+        for (int c0 = 0; c0 < n_chunks; c0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i)
+                v[i] = c0 + i < n_chunks ? chunk_counts[(size_t)(c0 + i) * E_local + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kB; ++i)
+                if (c0 + i < n_chunks) {
+                    chunk_counts[(size_t)(c0 + i) * E_local + e] = run;
+                    run += v[i];
+                }
         }
         tot[e] = run;
     }
@@ -73,7 +83,15 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int32_t* __restrict__ ch
         counts[e] = tot[e];
         offsets[e] = excl[e];
         const int o = excl[e];
-        for (int c = 0; c < n_chunks; ++c) chunk_counts[(size_t)c * E_local + e] += o;
+        for (int c0 = 0; c0 < n_chunks; c0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i)
+                v[i] = c0 + i < n_chunks ? chunk_counts[(size_t)(c0 + i) * E_local + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kB; ++i)
+                if (c0 + i < n_chunks) chunk_counts[(size_t)(c0 + i) * E_local + e] = v[i] + o;
+        }
     }
     if (e == 0) {
         counts[E_local] = n_shared;
