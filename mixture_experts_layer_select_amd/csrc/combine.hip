@@ -144,25 +144,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_small_k_kernel(
     for (; u < n_units; u += gridDim.x) {
         const int t = (int)(u / nch);
         const int h = (int)(u % nch) * kChunkH + threadIdx.x * 8;
-        // every row load is issued before the first sum, each through a
-        // descriptor of its (uniform) row: a non-local pick (row -1) or an
-        // absent shared row gets an empty range, so its load reads zeros
-        // without a memory request and its value is never used
-        float v[kSmallK][8], vs[8];
-        auto row_load = [&](int row, float* out8) {
-            const __amdgpu_buffer_rsrc_t rs =
-                buffer_rsrc(y + (size_t)(row > 0 ? row : 0) * H, row >= 0 ? (uint32_t)H * 2u : 0u);
-            const u32x4 q = buffer_load16(rs, (uint32_t)h * 2u, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                out8[2 * i] = bf16_lo(q[i]);
-                out8[2 * i + 1] = bf16_hi(q[i]);
-            }
-        };
+        // every row load is issued before the first sum; a non-local pick
+        // (row -1) or an absent shared row issues none (a uniform branch
+        // around the load only: the values are unpacked after all loads, so
+        // they stay in flight together)
+        u32x4 q[kSmallK], qs;
         if (h < H) {
 #pragma unroll
-            for (int j = 0; j < kSmallK; ++j) row_load(rows[j], v[j]);
-            row_load(shared0 >= 0 ? shared0 + t : -1, vs);
+            for (int j = 0; j < kSmallK; ++j)
+                if (rows[j] >= 0)
+                    q[j] = buffer_load16(buffer_rsrc(y + (size_t)rows[j] * H, (uint32_t)H * 2u),
+                                         (uint32_t)h * 2u, 0);
+            if (shared0 >= 0)
+                qs = buffer_load16(buffer_rsrc(y + (size_t)(shared0 + t) * H, (uint32_t)H * 2u),
+                                   (uint32_t)h * 2u, 0);
         }
         float wc[kSmallK];
         int rc[kSmallK];
@@ -178,11 +173,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_small_k_kernel(
             for (int j = 0; j < kSmallK; ++j)
                 if (rc[j] >= 0) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wc[j], v[j][i], acc[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] = __builtin_fmaf(wc[j], bf16_lo(q[j][i]), acc[2 * i]);
+                        acc[2 * i + 1] = __builtin_fmaf(wc[j], bf16_hi(q[j][i]), acc[2 * i + 1]);
+                    }
                 }
             if (shared0 >= 0) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += vs[i];
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += bf16_lo(qs[i]);
+                    acc[2 * i + 1] += bf16_hi(qs[i]);
+                }
             }
             store8(out + (size_t)t * H + h, acc);
         }
