@@ -436,8 +436,9 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
 // loads (global_load_lds_dwordx4) into a 3-stage ring, each stage its own
 // __shared__ object so the compiler can tell the stage being filled from the
 // one being read. Steps j+1 and j+2 are in flight while step j computes.
-// Every wave issues the same 9 loads per step (2 weight fragments x 2 halves,
-// 4 activation pieces, 1 scale piece), so one vmcnt value is exact for all.
+// Every wave issues the same 5 + NX loads per step (2 weight fragments x 2
+// halves, 1 scale piece, NX = 1, 2 or 4 activation pieces of 8 rows by the
+// tile's height), so one vmcnt value is exact for all.
 // An expert with up to 256 rows streams each weight byte once; larger ones
 // run their M tiles of one n-block side by side (item_at) and share it
 // through L2.
@@ -508,8 +509,14 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     const int i_hi = (int)((long)n_items * (xcd + 1) / 8);
 
     for (int item = i_lo + (blockIdx.x >> 3); item < i_hi; item += per_xcd) {
-        int nb;
-        const MTile tile = item_at(tm, offsets, n_groups, max_rows, item, NB, kLTM, nb);
+        int nb_v;
+        const MTile tile_v = item_at(tm, offsets, n_groups, max_rows, item, NB, kLTM, nb_v);
+        // the item is the same for every lane: scalar registers, scalar buffer
+        // descriptors and scalar branches on the tile's height
+        const int nb = __builtin_amdgcn_readfirstlane(nb_v);
+        const MTile tile{__builtin_amdgcn_readfirstlane(tile_v.group),
+                         __builtin_amdgcn_readfirstlane(tile_v.row0),
+                         __builtin_amdgcn_readfirstlane(tile_v.rows)};
         const bool routed = tile.group < n_routed;
         const uint8_t* Wg = routed ? W + (size_t)tile.group * Nw * K : Wsh;
         const float* Sg = routed ? Wsc + (size_t)tile.group * (Nw / kBK) * nk : Wsh_sc;
@@ -520,8 +527,10 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
             const int h = i / nk, kc = i % nk;
             wsc[h][kc] = Sg[(size_t)(h ? blk1 : blk0) * nk + kc];
         }
-        // this wave's weight fragments (A operand): 32-bit lane offsets from the
-        // item's (scalar) weight base, so the loads take the SGPR-base form
+        // Every load goes through a buffer descriptor of the item (scalar) with
+        // a 32-bit lane offset fixed for the item and the K step's offset in a
+        // scalar register, so the loop computes no per-lane addresses.
+        // This wave's weight fragments (A operand):
         uint32_t woff[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -532,7 +541,6 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
         const int wblk = kSwiGLU ? 0 : (wave >> 2);  // SwiGLU: s selects the block
         // activation pieces p = 8i + wave hold LDS rows 8p + [0,8); lane: row
         // 8p + lane/8 (clamped to the tile), physical chunk lane%8
-        const uint8_t* Xt = X + (size_t)tile.row0 * K;
         uint32_t xoff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -544,23 +552,27 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
         // scales: wave w loads rows 64(w%4) + lane (clamped) into xs[64w + lane]
         const int sr = 64 * (wave & 3) + lane;
         const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1);
-        const float* Xst = Xs + tile.row0;
         const int nms = (tile.rows + 15) >> 4;
+        const __amdgpu_buffer_rsrc_t wr_d = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K));
+        const __amdgpu_buffer_rsrc_t xr_d =
+            buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K));
+        const __amdgpu_buffer_rsrc_t sr_d = buffer_rsrc(
+            Xs + tile.row0, clamp_bytes(((size_t)(nk - 1) * max_rows + tile.rows) * 4));
 
         u32x8 wr[3][2];
-        auto issue = [&](int kc, auto slot_c, XStage& S) {
+        auto issue = [&](int kc, auto slot_c, XStage& S, auto nx_c) {
             constexpr int sl = decltype(slot_c)::value;
+            constexpr int NX = decltype(nx_c)::value;
             kc = kc < nk ? kc : nk - 1;
-            const uint8_t* xk = Xt + (size_t)kc * kBK;
+            const uint32_t ko = (uint32_t)kc * kBK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(xk + xoff[i], &S.x[(i * 8 + wave) * 1024]);
-            lds_dma4(Xst + (size_t)kc * max_rows + soff, &S.xs[64 * wave]);
-            const uint8_t* wk = Wg + (size_t)kc * kBK;
+            for (int i = 0; i < NX; ++i) lds_buf16(xr_d, xoff[i], ko, &S.x[(i * 8 + wave) * 1024]);
+            lds_buf4(sr_d, soff * 4, (uint32_t)kc * max_rows * 4, &S.xs[64 * wave]);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                wr[sl][s] = __builtin_shufflevector(*reinterpret_cast<const u32x4*>(wk + woff[s]),
-                                                    *reinterpret_cast<const u32x4*>(wk + woff[s] + 64),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
+                wr[sl][s] = __builtin_shufflevector(buffer_load16(wr_d, woff[s], ko),
+                                                    buffer_load16(wr_d, woff[s] + 64, ko), 0, 1, 2, 3,
+                                                    4, 5, 6, 7);
         };
 
         f32x4 acc[2][16];
@@ -628,91 +640,112 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
         // twelve steps per iteration, down (16) six: a longer body makes the
         // drains rarer, but its last iteration issues (clamped, unused) loads
         // for every step past the end.
-        issue(0, S0{}, st0);
-        issue(1, S1{}, st1);
-        if constexpr (kSwiGLU) {
-            for (int j = 0; j < nk; j += 12) {
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 2, S2{}, st2);
-                compute(j, S0{}, st0);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 3, S0{}, st0);
-                if (j + 1 < nk) compute(j + 1, S1{}, st1);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 4, S1{}, st1);
-                if (j + 2 < nk) compute(j + 2, S2{}, st2);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 5, S2{}, st2);
-                if (j + 3 < nk) compute(j + 3, S0{}, st0);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 6, S0{}, st0);
-                if (j + 4 < nk) compute(j + 4, S1{}, st1);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 7, S1{}, st1);
-                if (j + 5 < nk) compute(j + 5, S2{}, st2);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 8, S2{}, st2);
-                if (j + 6 < nk) compute(j + 6, S0{}, st0);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 9, S0{}, st0);
-                if (j + 7 < nk) compute(j + 7, S1{}, st1);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 10, S1{}, st1);
-                if (j + 8 < nk) compute(j + 8, S2{}, st2);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 11, S2{}, st2);
-                if (j + 9 < nk) compute(j + 9, S0{}, st0);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 12, S0{}, st0);
-                if (j + 10 < nk) compute(j + 10, S1{}, st1);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 13, S1{}, st1);
-                if (j + 11 < nk) compute(j + 11, S2{}, st2);
+        // The activation pieces a wave loads per step: 32 pieces of 8 rows cover
+        // 256 rows, so a tile of at most 64 (128) rows needs 8 (16) of them,
+        // one (two) per wave. Each variant issues the same 5 + NX loads per
+        // step in every wave, so its waits stay exact.
+        auto run = [&](auto nx_c) {
+            constexpr int NX = decltype(nx_c)::value;
+            issue(0, S0{}, st0, nx_c);
+            issue(1, S1{}, st1, nx_c);
+            if constexpr (kSwiGLU) {
+                for (int j = 0; j < nk; j += 12) {
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 2, S2{}, st2, nx_c);
+                    compute(j, S0{}, st0);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 3, S0{}, st0, nx_c);
+                    if (j + 1 < nk) compute(j + 1, S1{}, st1);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 4, S1{}, st1, nx_c);
+                    if (j + 2 < nk) compute(j + 2, S2{}, st2);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 5, S2{}, st2, nx_c);
+                    if (j + 3 < nk) compute(j + 3, S0{}, st0);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 6, S0{}, st0, nx_c);
+                    if (j + 4 < nk) compute(j + 4, S1{}, st1);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 7, S1{}, st1, nx_c);
+                    if (j + 5 < nk) compute(j + 5, S2{}, st2);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 8, S2{}, st2, nx_c);
+                    if (j + 6 < nk) compute(j + 6, S0{}, st0);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 9, S0{}, st0, nx_c);
+                    if (j + 7 < nk) compute(j + 7, S1{}, st1);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 10, S1{}, st1, nx_c);
+                    if (j + 8 < nk) compute(j + 8, S2{}, st2);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 11, S2{}, st2, nx_c);
+                    if (j + 9 < nk) compute(j + 9, S0{}, st0);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 12, S0{}, st0, nx_c);
+                    if (j + 10 < nk) compute(j + 10, S1{}, st1);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 13, S1{}, st1, nx_c);
+                    if (j + 11 < nk) compute(j + 11, S2{}, st2);
+                }
+            } else {
+                for (int j = 0; j < nk; j += 6) {
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 2, S2{}, st2, nx_c);
+                    compute(j, S0{}, st0);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 3, S0{}, st0, nx_c);
+                    if (j + 1 < nk) compute(j + 1, S1{}, st1);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 4, S1{}, st1, nx_c);
+                    if (j + 2 < nk) compute(j + 2, S2{}, st2);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 5, S2{}, st2, nx_c);
+                    if (j + 3 < nk) compute(j + 3, S0{}, st0);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 6, S0{}, st0, nx_c);
+                    if (j + 4 < nk) compute(j + 4, S1{}, st1);
+                    wait_vmcnt<5 + NX>();
+                    barrier_only();
+                    issue(j + 7, S1{}, st1, nx_c);
+                    if (j + 5 < nk) compute(j + 5, S2{}, st2);
+                }
             }
-        } else {
-            for (int j = 0; j < nk; j += 6) {
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 2, S2{}, st2);
-                compute(j, S0{}, st0);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 3, S0{}, st0);
-                if (j + 1 < nk) compute(j + 1, S1{}, st1);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 4, S1{}, st1);
-                if (j + 2 < nk) compute(j + 2, S2{}, st2);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 5, S2{}, st2);
-                if (j + 3 < nk) compute(j + 3, S0{}, st0);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 6, S0{}, st0);
-                if (j + 4 < nk) compute(j + 4, S1{}, st1);
-                wait_vmcnt<9>();
-                barrier_only();
-                issue(j + 7, S1{}, st1);
-                if (j + 5 < nk) compute(j + 5, S2{}, st2);
-            }
-        }
-        wait_vmcnt<0>();
+            wait_vmcnt<0>();
+        };
+        using X1 = std::integral_constant<int, 1>;
+        using X2 = std::integral_constant<int, 2>;
+        using X4 = std::integral_constant<int, 4>;
+        const int rows_u = __builtin_amdgcn_readfirstlane(tile.rows);
+        if (rows_u <= 64)
+            run(X1{});
+        else if (rows_u <= 128)
+            run(X2{});
+        else
+            run(X4{});
         __syncthreads();  // the ring and wsc are reused below and by the next item
 
         // epilogue: lane holds D[n = 16-row block s, row 4*lk + r4][m = ms*16 + li]
+        // (the token index is made opaque per item: hoisted out of the item loop,
+        // its 16 per-block copies would be spilled)
+        int li_e = li;
+        asm volatile("" : "+v"(li_e));
         if (kSwiGLU) {
 #pragma unroll
             for (int ms = 0; ms < 16; ++ms) {
@@ -724,13 +757,13 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
                 }
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                if (lk == 0) red[wave * kLTM + ms * 16 + li] = mx;
+                if (lk == 0) red[wave * kLTM + ms * 16 + li_e] = mx;
             }
             __syncthreads();
             uint8_t* codes = reinterpret_cast<uint8_t*>(out);
 #pragma unroll
             for (int ms = 0; ms < 16; ++ms) {
-                const int m = ms * 16 + li;
+                const int m = ms * 16 + li_e;
                 if (ms < nms && m < tile.rows) {
                     float mx = red[m];
 #pragma unroll
@@ -749,7 +782,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
             uint16_t* y = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
             for (int ms = 0; ms < 16; ++ms) {
-                const int m = ms * 16 + li;
+                const int m = ms * 16 + li_e;
                 if (ms < nms && m < tile.rows) {
                     uint16_t* orow = y + (size_t)(tile.row0 + m) * ldo;
 #pragma unroll
