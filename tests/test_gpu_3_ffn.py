@@ -105,6 +105,14 @@ def test_ffn_groups_across_the_tile_height(fmt):
     _run(fmt, 512, 256, [0, 257, 3, 513, 256, 700, 1, 0, 600], shared=True, seed=3)
 
 
+def test_ffn_fp8_small_group_heights():
+    """Small-group fp8 tiles on both sides of 64 and 128 rows (a tile loads one,
+    two or four 8-row activation pieces per wave and K step by its height) and
+    up to 256 rows, with K loops of exactly one unrolled body: H = 1536 gives
+    12 gate/up steps, I = 768 six down steps."""
+    _run("fp8", 1536, 768, [63, 64, 65, 127, 128, 129, 191, 193, 255, 256, 8], shared=True, seed=8)
+
+
 def test_ffn_fp8_large_groups_in_panels():
     """Groups of 6 and 9 256-row tiles (the large-group launch orders a
     group's items in panels of 4 m-tiles: one full panel and a 2-tile
