@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kBf16Oc
 // lane). Weight rows are private to a wave, so they stream from global memory
 // straight into a 3-slot register ring (MFMA A operand); the activation tile
 // of each K step (128), shared by all waves, arrives by direct global->LDS
-// loads (global_load_lds_dwordx4) into a 3-stage ring, each stage its own
+// loads (buffer_load_dwordx4 ... lds) into a 3-stage ring, each stage its own
 // __shared__ object so the compiler can tell the stage being filled from the
 // one being read. Steps j+1 and j+2 are in flight while step j computes.
 // Every wave issues the same 5 + NX loads per step (2 weight fragments x 2
@@ -463,14 +463,8 @@ struct XStage {
                             // duplicate scale loads of waves 4..7
 };
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
-}
-// the same through a buffer descriptor: a 32-bit lane offset plus a uniform
-// offset in a scalar register, no 64-bit address per lane
+// direct global->LDS loads through a buffer descriptor: a 32-bit lane offset
+// plus a uniform offset in a scalar register, no 64-bit address per lane
 __device__ __forceinline__ void lds_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                           void* l) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)l, 16, voff,
