@@ -351,7 +351,9 @@ __global__ __launch_bounds__(256) void perm_quant_tokens_fp8_kernel(
 // A workgroup copies 16 consecutive rows: their tokens go to LDS once, the
 // codes move as 16-byte chunks over all (row, chunk) pairs, eight loads in
 // flight per thread, and each scale block is written for 16 consecutive rows
-// at once.
+// at once. The copies are stored with the streaming (nontemporal) hint: the
+// routed rows are read back once per n-block much later, after more than the
+// caches hold (333 -> 306 us for R1's 16384-token batch).
 constexpr int kCopyRows = 16;
 __global__ __launch_bounds__(256) void perm_copy_fp8_kernel(
     const int32_t* __restrict__ row_to_slot, const int32_t* __restrict__ offsets, int E_local,
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(256) void perm_copy_fp8_kernel(
                 const int i = i0 + 256 * u;
                 if (i < total) {
                     const int rr = i / nc, c = i - rr * nc;
-                    *reinterpret_cast<u32x4*>(x_perm + (r0 + rr) * H + 16 * c) = v[u];
+                    __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(x_perm + (r0 + rr) * H + 16 * c));
                 }
             }
         }
