@@ -3,7 +3,10 @@
 A step is one pass of the whole layer through the C ABI -- moe_route (or,
 for batches of 4096 tokens and more, moe_route_select, which returns the same
 ids and weights), moe_permute, moe_expert_ffn_gate_up, moe_expert_ffn_down,
-moe_combine -- over one batch of synthetic tokens already resident in HBM. The default workload
+moe_combine -- over one batch of synthetic tokens already resident in HBM. fp8
+layers with a shared expert run moe_permute for the maps only, quantise each
+token once (moe_quantize_tokens) and read the token rows in gate/up
+(moe_expert_ffn_gate_up_tokens). The default workload
 is the R1 decode layer in bf16: 256 tokens, hidden 7168, 256 routed experts
 (intermediate 2048, top-8 by sigmoid score with Zipf(1.1)-skewed popularity)
 plus one shared expert. Other workloads (--config 3, 4, 5) are available for
@@ -287,12 +290,10 @@ def main():
         layer.permute(x, b, ids_in)
         if i is not None:
             ev[i][0].record(stream)
-        L.moe_expert_ffn_gate_up(layer.weights, b.x_perm, b.x_perm_scale, b.offsets, layer.n_groups,
-                                 cap, b.ws_ffn, b.ws_ffn.numel())
+        layer.gate_up(b)
         if i is not None:
             ev[i][1].record(stream)
-        L.moe_expert_ffn_down(layer.weights, b.offsets, layer.n_groups, cap, b.y_perm, b.ws_ffn,
-                              b.ws_ffn.numel())
+        layer.down(b)
         layer.combine(b, w_in)
 
     log(f"[bench] warmup {args.warmup}")

@@ -182,6 +182,32 @@ moe_status moe_expert_ffn_down(const moe_expert_weights* w, const int32_t* exper
                                int n_groups, int max_rows, void* y_perm, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* fp8 gate/up without a permuted copy of the activations ([Moreh-EP] Library
+ * optimization: the fused MoE kernel reads each expert's tokens itself):
+ * moe_quantize_tokens quantises every token once, and
+ * moe_expert_ffn_gate_up_tokens reads permuted row r's activations from its
+ * token's row, token = slot < T*k ? slot / k : slot - T*k with
+ * slot = row_to_slot[r] (moe_permute's map, which may then run with x_perm
+ * NULL). The result in the workspace is bit for bit the one moe_expert_ffn_gate_up
+ * computes from the x_perm moe_permute would write; moe_expert_ffn_down
+ * follows as usual.
+ *   moe_quantize_tokens: x [T, H] bf16 -> codes [T, H] e4m3 and scales
+ *   [H/128, T] fp32 (out, K-major), per 1x128 block exactly as moe_permute's
+ *   fp8 x_perm. Limits: H % 128 == 0, T*H < 2^31.
+ *   moe_expert_ffn_gate_up_tokens: x_tokens, x_tokens_scale as written by
+ *   moe_quantize_tokens; row_to_slot [max_rows] (device; rows below
+ *   offsets[n_groups] must hold slots in [0, T*k+T)); other arguments, limits
+ *   and workspace as for moe_expert_ffn_gate_up with dt = MOE_FP8_E4M3 only;
+ *   T*H < 2^31. A slot outside that range reads another token's row or
+ *   zeros, never memory outside the token buffers. */
+moe_status moe_quantize_tokens(const void* x, moe_dtype x_dt, int T, int H, void* codes,
+                               float* scales, void* stream);
+moe_status moe_expert_ffn_gate_up_tokens(const moe_expert_weights* w, const void* x_tokens,
+                                         const float* x_tokens_scale, int T, int k,
+                                         const int32_t* row_to_slot, const int32_t* expert_offsets,
+                                         int n_groups, int max_rows, void* workspace,
+                                         size_t ws_bytes, void* stream);
+
 /* Routing-weighted combine back to token order ([Moreh-EP] Overview:
  * dispatch/combine; the local half of it).
  *   out[t] = sum_{j: slot_to_row[t*k+j] >= 0} topk_w[t,j] * y_perm[slot_to_row[t*k+j]]

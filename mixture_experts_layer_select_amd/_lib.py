@@ -22,7 +22,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 EXPORTS = [
     "moe_route", "moe_route_select_workspace_size", "moe_route_select", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
-    "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_combine", "moe_balanced_partition", "moe_gather_rows",
+    "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_quantize_tokens",
+    "moe_expert_ffn_gate_up_tokens", "moe_combine", "moe_balanced_partition", "moe_gather_rows",
     "moe_count_accumulate", "moe_coactivation", "moe_affinity_partition",
     "moe_status_string", "moe_last_error_message",
 ]
@@ -66,6 +67,9 @@ def lib() -> C.CDLL:
         L.moe_expert_ffn.argtypes = [C.POINTER(moe_expert_weights), p, p, p, i, i, p, p, sz, p]
         L.moe_expert_ffn_gate_up.argtypes = [C.POINTER(moe_expert_weights), p, p, p, i, i, p, sz, p]
         L.moe_expert_ffn_down.argtypes = [C.POINTER(moe_expert_weights), p, i, i, p, p, sz, p]
+        L.moe_quantize_tokens.argtypes = [p, i, i, i, p, p, p]
+        L.moe_expert_ffn_gate_up_tokens.argtypes = [C.POINTER(moe_expert_weights), p, p, i, i, p, p, i, i,
+                                                    p, sz, p]
         L.moe_combine.argtypes = [p, i, p, p, i, i, i, p, i, p, i, p]
         L.moe_balanced_partition.argtypes = [p, i, i, p, p, p]
         L.moe_gather_rows.argtypes = [p, i, p, p, i, sz, p]
@@ -76,7 +80,7 @@ def lib() -> C.CDLL:
         L.moe_status_string.restype = C.c_char_p
         L.moe_last_error_message.restype = C.c_char_p
         for f in ("moe_route", "moe_route_select", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_gate_up",
-                  "moe_expert_ffn_down", "moe_combine",
+                  "moe_expert_ffn_down", "moe_quantize_tokens", "moe_expert_ffn_gate_up_tokens", "moe_combine",
                   "moe_balanced_partition", "moe_gather_rows", "moe_count_accumulate",
                   "moe_coactivation", "moe_affinity_partition"):
             getattr(L, f).restype = C.c_int
@@ -150,8 +154,12 @@ def moe_permute(topk_ids, T, k, expert_base, E_local, include_shared, x, x_dt, H
 
 def make_weights(dt, E_local, H, I, w13, w2, w13_scale=None, w2_scale=None, ws13=None, ws2=None,
                  ws13_scale=None, ws2_scale=None) -> moe_expert_weights:
-    return moe_expert_weights(dt, E_local, H, I, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
-                              _ptr(ws13), _ptr(ws13_scale), _ptr(ws2), _ptr(ws2_scale))
+    w = moe_expert_weights(dt, E_local, H, I, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                           _ptr(ws13), _ptr(ws13_scale), _ptr(ws2), _ptr(ws2_scale))
+    # the struct holds raw device pointers: keep the tensors alive with it, or
+    # their memory could be handed to other tensors while the struct is in use
+    w._tensors = (w13, w2, w13_scale, w2_scale, ws13, ws2, ws13_scale, ws2_scale)
+    return w
 
 
 def moe_expert_ffn_workspace_size(w: moe_expert_weights, max_rows: int) -> int:
@@ -170,6 +178,18 @@ def moe_expert_ffn_gate_up(w: moe_expert_weights, x_perm, x_perm_scale, expert_o
     _check("moe_expert_ffn_gate_up", lib().moe_expert_ffn_gate_up(
         C.byref(w), _ptr(x_perm), _ptr(x_perm_scale), _ptr(expert_offsets), n_groups, max_rows,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_quantize_tokens(x, x_dt, T, H, codes, scales, stream=None):
+    _check("moe_quantize_tokens", lib().moe_quantize_tokens(
+        _ptr(x), x_dt, T, H, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_expert_ffn_gate_up_tokens(w: moe_expert_weights, x_tokens, x_tokens_scale, T, k, row_to_slot,
+                                  expert_offsets, n_groups, max_rows, workspace, ws_bytes, stream=None):
+    _check("moe_expert_ffn_gate_up_tokens", lib().moe_expert_ffn_gate_up_tokens(
+        C.byref(w), _ptr(x_tokens), _ptr(x_tokens_scale), T, k, _ptr(row_to_slot),
+        _ptr(expert_offsets), n_groups, max_rows, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def moe_expert_ffn_down(w: moe_expert_weights, expert_offsets, n_groups, max_rows, y_perm, workspace,

@@ -220,6 +220,38 @@ moe_status moe_expert_ffn_gate_up(const moe_expert_weights* w, const void* x_per
                               (hipStream_t)stream);
 }
 
+moe_status moe_quantize_tokens(const void* x, moe_dtype x_dt, int T, int H, void* codes,
+                               float* scales, void* stream) {
+    g_msg[0] = 0;
+    REQUIRE(T >= 0 && H >= 1, MOE_ERR_INVALID_ARG, "moe_quantize_tokens: T=%d H=%d", T, H);
+    REQUIRE(x_dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "moe_quantize_tokens: x must be bf16");
+    REQUIRE(H % 128 == 0, MOE_ERR_UNSUPPORTED, "moe_quantize_tokens: H=%d not a multiple of 128", H);
+    REQUIRE((long)T * H < (1L << 31), MOE_ERR_UNSUPPORTED, "moe_quantize_tokens: T*H >= 2^31");
+    if (T == 0) return MOE_OK;
+    REQUIRE(x && codes && scales, MOE_ERR_INVALID_ARG, "moe_quantize_tokens: null pointer");
+    return launch_quantize_tokens(x, T, H, codes, scales, (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn_gate_up_tokens(const moe_expert_weights* w, const void* x_tokens,
+                                         const float* x_tokens_scale, int T, int k,
+                                         const int32_t* row_to_slot, const int32_t* expert_offsets,
+                                         int n_groups, int max_rows, void* workspace,
+                                         size_t ws_bytes, void* stream) {
+    g_msg[0] = 0;
+    moe_status s = check_ffn_call("moe_expert_ffn_gate_up_tokens", w, n_groups, max_rows,
+                                  expert_offsets, workspace, ws_bytes);
+    if (s) return s;
+    REQUIRE(w->dt == MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED, "moe_expert_ffn_gate_up_tokens: fp8 only");
+    REQUIRE(T >= 0 && k >= 1, MOE_ERR_INVALID_ARG, "moe_expert_ffn_gate_up_tokens: T=%d k=%d", T, k);
+    REQUIRE((long)T * w->H < (1L << 31) && (long)T * (k + 1) < (1L << 31), MOE_ERR_UNSUPPORTED,
+            "moe_expert_ffn_gate_up_tokens: T*H or T*(k+1) >= 2^31");
+    if (max_rows == 0 || T == 0) return MOE_OK;
+    REQUIRE(x_tokens && x_tokens_scale && row_to_slot, MOE_ERR_INVALID_ARG,
+            "moe_expert_ffn_gate_up_tokens: null pointer");
+    return launch_ffn_gate_up(w, x_tokens, x_tokens_scale, expert_offsets, n_groups, max_rows,
+                              workspace, (hipStream_t)stream, ActSrc{row_to_slot, k, T * k, T, T});
+}
+
 moe_status moe_expert_ffn_down(const moe_expert_weights* w, const int32_t* expert_offsets,
                                int n_groups, int max_rows, void* y_perm, void* workspace,
                                size_t ws_bytes, void* stream) {

@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
     const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
     int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
-    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
+    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo, ActSrc src) {
     __shared__ __attribute__((aligned(1024))) XStage st0;
     __shared__ __attribute__((aligned(1024))) XStage st1;
     __shared__ __attribute__((aligned(1024))) XStage st2;
@@ -535,23 +535,36 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
         const int wblk = kSwiGLU ? 0 : (wave >> 2);  // SwiGLU: s selects the block
         // activation pieces p = 8i + wave hold LDS rows 8p + [0,8); lane: row
         // 8p + lane/8 (clamped to the tile), physical chunk lane%8
+        // Activation rows: rows of the tile in x_perm (offsets from the tile's
+        // first row), or their tokens' rows in a token buffer (offsets from
+        // its start).
+        const bool gather = src.row_slot != nullptr;
+        auto src_row = [&](int rr) -> int {
+            if (!gather) return rr;
+            const int slot = src.row_slot[tile.row0 + rr];
+            return slot < src.S ? slot / src.k : slot - src.S;
+        };
         uint32_t xoff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = (i * 8 + wave) * 8 + (lane >> 3);
             const int rr = r < tile.rows ? r : tile.rows - 1;
             const int c = (lane & 7) ^ ((r >> 1) & 7);
-            xoff[i] = (uint32_t)rr * K + c * 16;
+            xoff[i] = (uint32_t)src_row(rr) * K + c * 16;
         }
         // scales: wave w loads rows 64(w%4) + lane (clamped) into xs[64w + lane]
         const int sr = 64 * (wave & 3) + lane;
-        const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1);
+        const uint32_t soff = (uint32_t)src_row(sr < tile.rows ? sr : tile.rows - 1);
+        const int s_ld = gather ? src.s_ld : max_rows;
         const int nms = (tile.rows + 15) >> 4;
         const __amdgpu_buffer_rsrc_t wr_d = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K));
         const __amdgpu_buffer_rsrc_t xr_d =
-            buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K));
-        const __amdgpu_buffer_rsrc_t sr_d = buffer_rsrc(
-            Xs + tile.row0, clamp_bytes(((size_t)(nk - 1) * max_rows + tile.rows) * 4));
+            gather ? buffer_rsrc(X, clamp_bytes((size_t)src.rows * K))
+                   : buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K));
+        const __amdgpu_buffer_rsrc_t sr_d =
+            gather ? buffer_rsrc(Xs, clamp_bytes(((size_t)(nk - 1) * s_ld + src.rows) * 4))
+                   : buffer_rsrc(Xs + tile.row0,
+                                 clamp_bytes(((size_t)(nk - 1) * max_rows + tile.rows) * 4));
 
         u32x8 wr[3][2];
         auto issue = [&](int kc, auto slot_c, XStage& S, auto nx_c) {
@@ -561,7 +574,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
             const uint32_t ko = (uint32_t)kc * kBK;
 #pragma unroll
             for (int i = 0; i < NX; ++i) lds_buf16(xr_d, xoff[i], ko, &S.x[(i * 8 + wave) * 1024]);
-            lds_buf4(sr_d, soff * 4, (uint32_t)kc * max_rows * 4, &S.xs[64 * wave]);
+            lds_buf4(sr_d, soff * 4, (uint32_t)kc * s_ld * 4, &S.xs[64 * wave]);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 wr[sl][s] = __builtin_shufflevector(buffer_load16(wr_d, woff[s], ko),
@@ -822,12 +835,12 @@ struct BigStage {
     float xs[kGTM];         // activation scales of the step
 };
 
-template <bool kSwiGLU>
+template <bool kSwiGLU, bool kGather>
 __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
     const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
     int n_routed, const int32_t* __restrict__ offsets, int n_groups, int max_rows, int K, int Nw,
-    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo) {
+    int NB, void* __restrict__ out, float* __restrict__ out_scale, int ldo, ActSrc src) {
     __shared__ __attribute__((aligned(1024))) BigStage st0;
     __shared__ __attribute__((aligned(1024))) BigStage st1;
     __shared__ TileMap tm;
@@ -874,11 +887,30 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         // time, so one lane offset of each kind stays live through the loop
         const int q0 = wave * 8 + (lane >> 3);
         const int c16 = ((lane & 7) ^ ((q0 >> 1) & 7)) * 16;
+        // kGather: activation rows are the tokens' rows of a token buffer,
+        // token = slot < S ? slot / k : slot - S for slot = row_slot[row];
+        // their four lane offsets are fixed for the item
+        auto src_row = [&](int rr) -> int {
+            const int slot = src.row_slot[tile.row0 + rr];
+            return slot < src.S ? slot / src.k : slot - src.S;
+        };
+        uint32_t xg[kGather ? 4 : 1];
+        if constexpr (kGather) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = q0 + 64 * i;
+                xg[i] = (uint32_t)src_row(r < tile.rows ? r : tile.rows - 1) * K + c16;
+            }
+        }
+        const int s_ld = kGather ? src.s_ld : max_rows;
         const __amdgpu_buffer_rsrc_t wr_d = buffer_rsrc(Wg, clamp_bytes((size_t)Nw * K));
         const __amdgpu_buffer_rsrc_t xr_d =
-            buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K));
-        const __amdgpu_buffer_rsrc_t sr_d = buffer_rsrc(
-            Xs + tile.row0, clamp_bytes(((size_t)(nk - 1) * max_rows + tile.rows) * 4));
+            kGather ? buffer_rsrc(X, clamp_bytes((size_t)src.rows * K))
+                    : buffer_rsrc(X + (size_t)tile.row0 * K, clamp_bytes((size_t)tile.rows * K));
+        const __amdgpu_buffer_rsrc_t sr_d =
+            kGather ? buffer_rsrc(Xs, clamp_bytes(((size_t)(nk - 1) * s_ld + src.rows) * 4))
+                    : buffer_rsrc(Xs + tile.row0,
+                                  clamp_bytes(((size_t)(nk - 1) * max_rows + tile.rows) * 4));
         const uint32_t woff0 = (uint32_t)(kSwiGLU ? nb * 128 + q0 : nb * 256 + q0) * K + c16;
         auto wdist = [&](int i) -> uint32_t {  // uniform: piece i's weight row - piece 0's
             if (kSwiGLU) return (uint32_t)(i < 2 ? 64 * i : Nw / 2 + 64 * (i - 2)) * K;
@@ -886,7 +918,8 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
         };
         // scales: waves 0..3 load rows 64w + lane (clamped to the tile)
         const int sr = 64 * wave + lane;
-        const uint32_t soff = (uint32_t)(sr < tile.rows ? sr : tile.rows - 1) * 4;
+        const int sr_c = sr < tile.rows ? sr : tile.rows - 1;
+        const uint32_t soff = (uint32_t)(kGather ? src_row(sr_c) : sr_c) * 4;
         const bool s_on = wave < 4 && 64 * wave < tile.rows;
         const int nms = max(0, min(8, (tile.rows - wm * 128 + 15) >> 4));
 
@@ -898,10 +931,11 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_big_kernel(
             for (int i = 0; i < 4; ++i)
                 if (64 * i + 8 * wave < tile.rows) {
                     const int r = q0 + 64 * i;
-                    const uint32_t xo = (uint32_t)(r < tile.rows ? r : tile.rows - 1) * K + c16;
+                    const uint32_t xo =
+                        kGather ? xg[i] : (uint32_t)(r < tile.rows ? r : tile.rows - 1) * K + c16;
                     lds_buf16(xr_d, xo, ko, &S.x[(i * 8 + wave) * 1024]);
                 }
-            if (s_on) lds_buf4(sr_d, soff, (uint32_t)kc * max_rows * 4, &S.xs[64 * wave]);
+            if (s_on) lds_buf4(sr_d, soff, (uint32_t)kc * s_ld * 4, &S.xs[64 * wave]);
         };
 
         f32x4 acc[4][8];
@@ -1163,7 +1197,9 @@ size_t ffn_workspace_bytes(const moe_expert_weights* w, int max_rows) {
 
 moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                               const float* x_perm_scale, const int32_t* offsets, int n_groups,
-                              int max_rows, void* ws, hipStream_t st) {
+                              int max_rows, void* ws, hipStream_t st, const ActSrc& src) {
+    if (src.row_slot && w->dt != MOE_FP8_E4M3)
+        return set_error(MOE_ERR_UNSUPPORTED, "gate/up from token rows: fp8 only");
     FfnWs s = carve(w, max_rows, ws);
     const int H = w->H, I = w->I, E = w->E_local;
     if (w->dt == MOE_F32) {
@@ -1197,15 +1233,22 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                            dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
                            (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
                            w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale,
-                           I);
+                           I, src);
         moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<gate_up>");
         if (r) return r;
         const long tl = 2L * max_rows / kGTM + 1;  // tiles of groups above 256 rows
-        hipLaunchKernelGGL(ffn_gemm_fp8_big_kernel<true>, dim3(persistent_grid_xcd(tl * NB, 1)),
-                           dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
-                           (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
-                           w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale,
-                           I);
+        if (src.row_slot)
+            hipLaunchKernelGGL((ffn_gemm_fp8_big_kernel<true, true>), dim3(persistent_grid_xcd(tl * NB, 1)),
+                               dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
+                               (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
+                               w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a,
+                               s.a_scale, I, src);
+        else
+            hipLaunchKernelGGL((ffn_gemm_fp8_big_kernel<true, false>), dim3(persistent_grid_xcd(tl * NB, 1)),
+                               dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
+                               (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
+                               w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a,
+                               s.a_scale, I, src);
         return check_launch("ffn_gemm_fp8_big_kernel<gate_up>");
     }
     return set_error(MOE_ERR_UNSUPPORTED, "fp8 gate/up: H=%d exceeds %d", H, kLMaxSteps * kBK);
@@ -1244,14 +1287,14 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
         hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<false>, dim3(persistent_grid_xcd((long)n_groups * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
                            w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
-                           max_rows, I, H, NB, y_perm, nullptr, H);
+                           max_rows, I, H, NB, y_perm, nullptr, H, ActSrc{nullptr, 0, 0, 0, 0});
         moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<down>");
         if (r) return r;
         const long tl = 2L * max_rows / kGTM + 1;
-        hipLaunchKernelGGL(ffn_gemm_fp8_big_kernel<false>, dim3(persistent_grid_xcd(tl * NB, 1)),
+        hipLaunchKernelGGL((ffn_gemm_fp8_big_kernel<false, false>), dim3(persistent_grid_xcd(tl * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
                            w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
-                           max_rows, I, H, NB, y_perm, nullptr, H);
+                           max_rows, I, H, NB, y_perm, nullptr, H, ActSrc{nullptr, 0, 0, 0, 0});
         return check_launch("ffn_gemm_fp8_big_kernel<down>");
     }
     return set_error(MOE_ERR_UNSUPPORTED, "fp8 down: I=%d exceeds %d", I, kLMaxSteps * kBK);

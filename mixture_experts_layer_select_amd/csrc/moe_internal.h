@@ -91,9 +91,20 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_loca
                           void* x_perm, float* x_perm_scale, void* ws, hipStream_t st);
 
 size_t ffn_workspace_bytes(const moe_expert_weights* w, int max_rows);
+// Where the fp8 gate/up GEMM reads permuted row r's activations: row r of
+// x_perm (row_slot null), or the row of its token in a [rows][H] token
+// buffer, token = slot < S ? slot / k : slot - S with slot = row_slot[r];
+// the scales are K-major with s_ld rows per K block.
+struct ActSrc {
+    const int32_t* row_slot;
+    int k, S, rows, s_ld;
+};
 moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                               const float* x_perm_scale, const int32_t* offsets, int n_groups,
-                              int max_rows, void* ws, hipStream_t st);
+                              int max_rows, void* ws, hipStream_t st,
+                              const ActSrc& src = ActSrc{nullptr, 0, 0, 0, 0});
+moe_status launch_quantize_tokens(const void* x, int T, int H, void* codes, float* scales,
+                                  hipStream_t st);
 moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, int n_groups,
                            int max_rows, void* y_perm, void* ws, hipStream_t st);
 

@@ -351,9 +351,7 @@ __global__ __launch_bounds__(256) void perm_quant_tokens_fp8_kernel(
 // A workgroup copies 16 consecutive rows: their tokens go to LDS once, the
 // codes move as 16-byte chunks over all (row, chunk) pairs, eight loads in
 // flight per thread, and each scale block is written for 16 consecutive rows
-// at once. The copies are stored with the streaming (nontemporal) hint: the
-// routed rows are read back once per n-block much later, after more than the
-// caches hold (333 -> 306 us for R1's 16384-token batch).
+// at once.
 constexpr int kCopyRows = 16;
 __global__ __launch_bounds__(256) void perm_copy_fp8_kernel(
     const int32_t* __restrict__ row_to_slot, const int32_t* __restrict__ offsets, int E_local,
@@ -392,14 +390,31 @@ __global__ __launch_bounds__(256) void perm_copy_fp8_kernel(
                 const int i = i0 + 256 * u;
                 if (i < total) {
                     const int rr = i / nc, c = i - rr * nc;
-                    __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(x_perm + (r0 + rr) * H + 16 * c));
+                    *reinterpret_cast<u32x4*>(x_perm + (r0 + rr) * H + 16 * c) = v[u];
                 }
             }
         }
     }
 }
 
+// every token quantised once into row t of a [T][H] token buffer, scales
+// K-major [H/128][T]
+__global__ __launch_bounds__(256) void quant_tokens_fp8_kernel(const uint16_t* __restrict__ x, int T,
+                                                               int H, uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales) {
+    for (long t = blockIdx.x; t < T; t += gridDim.x) quant_row_fp8(x + t * H, H, T, t, codes, scales);
+}
+
 }  // namespace
+
+moe_status launch_quantize_tokens(const void* x, int T, int H, void* codes, float* scales,
+                                  hipStream_t st) {
+    if (T == 0) return MOE_OK;
+    const int blocks = (int)std::min<long>(T, (long)device_info().cu_count * 8);
+    hipLaunchKernelGGL(quant_tokens_fp8_kernel, dim3(blocks), dim3(256), 0, st, (const uint16_t*)x, T,
+                       H, (uint8_t*)codes, scales);
+    return check_launch("quant_tokens_fp8_kernel");
+}
 
 static moe_status launch_gather(const void* x, moe_dtype x_dt, int H, moe_dtype perm_dt,
                                 const int32_t* row_to_slot, const int32_t* offsets, int E_local,

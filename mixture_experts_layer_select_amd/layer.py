@@ -27,13 +27,15 @@ class LayerBuffers:
     offsets: torch.Tensor
     row_to_slot: torch.Tensor
     slot_to_row: torch.Tensor
-    x_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor]  # None when fp8 gate/up reads the token rows
     x_perm_scale: Optional[torch.Tensor]
     y_perm: torch.Tensor
     out: torch.Tensor
     ws_perm: torch.Tensor
     ws_ffn: torch.Tensor
     ws_route: Optional[torch.Tensor] = None  # moe_route_select's workspace (large batches)
+    x_tok: Optional[torch.Tensor] = None  # fp8 token codes [T, H] (moe_quantize_tokens)
+    x_tok_scale: Optional[torch.Tensor] = None  # their scales [H/128, T]
 
 
 class MoELayer:
@@ -63,6 +65,17 @@ class MoELayer:
                                       sh.get("w2_scale"))
         self.n_groups = self.E_local + (1 if shared is not None else 0)
         self._bufs = {}
+
+    # fp8 layers with a shared expert quantise each token once and let gate/up
+    # read its token's row (moe_quantize_tokens + moe_expert_ffn_gate_up_tokens)
+    # instead of copying every routed row into x_perm; the result is the same
+    # bit for bit. Without a shared group moe_permute quantises each routed row
+    # straight from x in one pass, and gate/up on the contiguous rows is faster
+    # than the gathered reads.
+    FP8_FROM_TOKENS = True
+
+    def uses_tokens(self) -> bool:
+        return self.fmt == "fp8" and self.FP8_FROM_TOKENS and self.shared is not None
 
     # Batches of at least this many tokens route through moe_route_select
     # (same ids and weights as moe_route; faster once the MFMA pass has a few
@@ -101,13 +114,17 @@ class MoELayer:
             offsets=torch.empty(self.E_local + 2, **i32),
             row_to_slot=torch.empty(cap, **i32),
             slot_to_row=torch.empty(T * k, **i32),
-            x_perm=torch.empty((cap, H), dtype=xdt, device=device),
-            x_perm_scale=torch.empty((H // 128, cap), **f32) if self.fmt == "fp8" else None,
+            x_perm=None if self.uses_tokens() else torch.empty((cap, H), dtype=xdt, device=device),
+            x_perm_scale=(torch.empty((H // 128, cap), **f32)
+                          if self.fmt == "fp8" and not self.uses_tokens() else None),
             y_perm=torch.empty((cap, H), dtype=act, device=device),
             out=torch.empty((T, H), dtype=act, device=device),
             ws_perm=torch.empty(max(ws_p, 1), dtype=torch.uint8, device=device),
             ws_ffn=torch.empty(max(ws_f, 1), dtype=torch.uint8, device=device),
         )
+        if self.uses_tokens():
+            b.x_tok = torch.empty((T, H), dtype=torch.uint8, device=device)
+            b.x_tok_scale = torch.empty((H // 128, T), **f32)
         if self.uses_route_select(T):
             b.ws_route = torch.empty(L.moe_route_select_workspace_size(T, E), dtype=torch.uint8,
                                      device=device)
@@ -134,11 +151,27 @@ class MoELayer:
                       self.act_dt, self.H, self.dt if self.fmt == "fp8" else self.act_dt, b.counts,
                       b.offsets, b.row_to_slot, b.slot_to_row, b.x_perm, b.x_perm_scale, b.ws_perm,
                       b.ws_perm.numel(), stream)
+        if self.uses_tokens():
+            L.moe_quantize_tokens(x, self.act_dt, T, self.H, b.x_tok, b.x_tok_scale, stream)
+
+    def gate_up(self, b: LayerBuffers, stream=None):
+        cap = b.T * self.k + b.T
+        if self.uses_tokens():
+            L.moe_expert_ffn_gate_up_tokens(self.weights, b.x_tok, b.x_tok_scale, b.T, self.k,
+                                            b.row_to_slot, b.offsets, self.n_groups, cap, b.ws_ffn,
+                                            b.ws_ffn.numel(), stream)
+        else:
+            L.moe_expert_ffn_gate_up(self.weights, b.x_perm, b.x_perm_scale, b.offsets,
+                                     self.n_groups, cap, b.ws_ffn, b.ws_ffn.numel(), stream)
+
+    def down(self, b: LayerBuffers, stream=None):
+        cap = b.T * self.k + b.T
+        L.moe_expert_ffn_down(self.weights, b.offsets, self.n_groups, cap, b.y_perm, b.ws_ffn,
+                              b.ws_ffn.numel(), stream)
 
     def ffn(self, b: LayerBuffers, stream=None):
-        cap = b.T * self.k + b.T
-        L.moe_expert_ffn(self.weights, b.x_perm, b.x_perm_scale, b.offsets, self.n_groups, cap,
-                         b.y_perm, b.ws_ffn, b.ws_ffn.numel(), stream)
+        self.gate_up(b, stream)
+        self.down(b, stream)
 
     def combine(self, b: LayerBuffers, topk_w=None, stream=None):
         w = b.topk_w if topk_w is None else topk_w
