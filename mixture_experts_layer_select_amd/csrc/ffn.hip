@@ -478,7 +478,7 @@ __device__ __forceinline__ void lds_buf4(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ ((r >> 1) & 7)) * 16; }
 
 
-template <bool kSwiGLU>
+template <bool kSwiGLU, bool kGather>
 __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ Xs, const uint8_t* __restrict__ W,
     const float* __restrict__ Wsc, const uint8_t* __restrict__ Wsh, const float* __restrict__ Wsh_sc,
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kLThreads) void ffn_gemm_fp8_lds_kernel(
         // Activation rows: rows of the tile in x_perm (offsets from the tile's
         // first row), or their tokens' rows in a token buffer (offsets from
         // its start).
-        const bool gather = src.row_slot != nullptr;
+        constexpr bool gather = kGather;
         auto src_row = [&](int rr) -> int {
             if (!gather) return rr;
             const int slot = src.row_slot[tile.row0 + rr];
@@ -1229,11 +1229,18 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
     const int NB = I / 128;
     if (H / kBK <= kLMaxSteps) {  // LDS-ring kernels: the item's weight scales fit the step table
         // groups of at most 256 rows (one tile each), then the larger ones
-        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<true>, dim3(persistent_grid_xcd((long)n_groups * NB, 1)),
-                           dim3(kLThreads), 0, st, (const uint8_t*)x_perm, x_perm_scale,
-                           (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->ws13,
-                           w->ws13_scale, E, offsets, n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale,
-                           I, src);
+        if (src.row_slot)
+            hipLaunchKernelGGL((ffn_gemm_fp8_lds_kernel<true, true>),
+                               dim3(persistent_grid_xcd((long)n_groups * NB, 1)), dim3(kLThreads), 0, st,
+                               (const uint8_t*)x_perm, x_perm_scale, (const uint8_t*)w->w13,
+                               w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E, offsets,
+                               n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale, I, src);
+        else
+            hipLaunchKernelGGL((ffn_gemm_fp8_lds_kernel<true, false>),
+                               dim3(persistent_grid_xcd((long)n_groups * NB, 1)), dim3(kLThreads), 0, st,
+                               (const uint8_t*)x_perm, x_perm_scale, (const uint8_t*)w->w13,
+                               w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E, offsets,
+                               n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale, I, src);
         moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<gate_up>");
         if (r) return r;
         const long tl = 2L * max_rows / kGTM + 1;  // tiles of groups above 256 rows
@@ -1284,7 +1291,7 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
     }
     const int NB = H / 256;
     if (I / kBK <= kLMaxSteps) {
-        hipLaunchKernelGGL(ffn_gemm_fp8_lds_kernel<false>, dim3(persistent_grid_xcd((long)n_groups * NB, 1)),
+        hipLaunchKernelGGL((ffn_gemm_fp8_lds_kernel<false, false>), dim3(persistent_grid_xcd((long)n_groups * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,
                            w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
                            max_rows, I, H, NB, y_perm, nullptr, H, ActSrc{nullptr, 0, 0, 0, 0});
