@@ -133,3 +133,35 @@ def test_gate_up_tokens_rejects_non_fp8():
     with pytest.raises(L.MoEError) as e:
         L.moe_expert_ffn_gate_up_tokens(w, x, xs, 4, 2, r2s, off, 2, 12, ws, ws_n)
     assert e.value.status == "MOE_ERR_UNSUPPORTED"
+
+
+def test_quantize_tokens_and_gate_up_tokens_empty_cases():
+    """T = 0 is a no-op for both calls; rows routed elsewhere (an expert-parallel
+    share that receives nothing) leave every group empty and A untouched."""
+    import mixture_experts_layer_select_amd as L
+    H, I, E_local, T, k = 256, 128, 4, 9, 2
+    cfg = mi.scaled(mi.CONFIGS[4], H=H, I=I, cid=460)
+    st = mi.stacked_expert_weights(cfg, range(E_local), device=DEV)
+    w = L.make_weights(L.FP8_E4M3, E_local, H, I, st["w13"], st["w2"], st["w13_scale"], st["w2_scale"])
+    codes = torch.zeros((1, H), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((H // 128, 1), dtype=torch.float32, device=DEV)
+    L.moe_quantize_tokens(codes, L.BF16, 0, H, codes, scales)  # T = 0: nothing is read or written
+    ids = torch.full((T, k), 40, dtype=torch.int32, device=DEV)  # outside the local experts
+    cap = T * k + T
+    i32 = dict(dtype=torch.int32, device=DEV)
+    counts, offsets = torch.empty(E_local + 1, **i32), torch.empty(E_local + 2, **i32)
+    r2s, s2r = torch.empty(cap, **i32), torch.empty(T * k, **i32)
+    wsp_n = L.moe_permute_workspace_size(T, k, E_local)
+    wsp = torch.empty(wsp_n, dtype=torch.uint8, device=DEV)
+    L.moe_permute(ids, T, k, 0, E_local, False, None, L.BF16, H, L.FP8_E4M3, counts, offsets, r2s, s2r,
+                  None, None, wsp, wsp_n)
+    x = mi.normal((T, H), 1.0, 461, DEV, torch.bfloat16)
+    xt = torch.empty((T, H), dtype=torch.uint8, device=DEV)
+    xts = torch.empty((H // 128, T), dtype=torch.float32, device=DEV)
+    L.moe_quantize_tokens(x, L.BF16, T, H, xt, xts)
+    ws_n = L.moe_expert_ffn_workspace_size(w, cap)
+    ws = torch.full((ws_n,), 0xA5, dtype=torch.uint8, device=DEV)
+    L.moe_expert_ffn_gate_up_tokens(w, xt, xts, T, k, r2s, offsets, E_local, cap, ws, ws_n)
+    torch.cuda.synchronize()
+    assert int(offsets[E_local].item()) == 0
+    assert bool((ws == 0xA5).all())
