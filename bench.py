@@ -6,17 +6,22 @@ ids and weights), moe_permute, moe_expert_ffn_gate_up, moe_expert_ffn_down,
 moe_combine -- over one batch of synthetic tokens already resident in HBM. fp8
 layers with a shared expert run moe_permute for the maps only, quantise each
 token once (moe_quantize_tokens) and read the token rows in gate/up
-(moe_expert_ffn_gate_up_tokens). The default workload
-is the R1 decode layer in bf16: 256 tokens, hidden 7168, 256 routed experts
-(intermediate 2048, top-8 by sigmoid score with Zipf(1.1)-skewed popularity)
-plus one shared expert. Other workloads (--config 3, 4, 5) are available for
-measurement; only the default run is the headline line.
+(moe_expert_ffn_gate_up_tokens).
+
+The headline workload is the largest single-GPU shape: the R1 layer on a
+large batch in fp8 (16384 tokens, hidden 7168, 256 routed experts of
+intermediate 2048, top-8 by sigmoid score with Zipf(1.1)-skewed popularity,
+one shared expert; e4m3 weights with 128x128 block scales, activations
+quantised per 1x128 block), MFMA-bound. The R1 decode layer in bf16 (256
+tokens, same experts, HBM-bound) is measured in the same process afterwards
+and reported under "decode" in the same line (--decode-config 0 skips it).
+Other workloads (--config 2, 3, 5) can be measured on their own.
 
 Printed: one JSON line with tokens/s, the roofline of the dominant kernel
-(the gate/up grouped GEMM: algorithmic bytes per launch over its average
-duration, timed with HIP events on the launch stream inside the timed
-region) and the CPU oracle's throughput on a bounded sample of the same
-workload.
+(the gate/up grouped GEMM: algorithmic flops or bytes per launch over its
+average duration, timed with HIP events on the launch stream inside the
+timed region) and the CPU oracle's throughput on a bounded sample of the
+headline workload.
 """
 from __future__ import annotations
 
@@ -43,7 +48,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4, 5])
+    ap.add_argument("--decode-config", type=int, default=2, choices=[0, 2, 3, 5],
+                    help="second workload timed in the same process after the first and "
+                         "reported under 'decode' (0 = none)")
     ap.add_argument("--cpu-sample", type=int, default=256,
                     help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -261,23 +269,17 @@ def cpu_baseline(cfg, layer, b, x, st, sh, topk, n_sample):
                       f"scaled per token"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer runs on one "
-              "GPU's share and uses no collectives.", file=sys.stderr)
-        sys.exit(2)
+def measure(cid: int, args, dev: str, with_cpu: bool) -> dict:
+    """Time one workload (warm-up, then args.steps whole-layer steps) and
+    return its JSON fields."""
     import numpy as np
     import torch
     import mixture_experts_layer_select_amd as L
 
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    log(f"[bench] building workload config {args.config}")
-    cfg, layer, x, st, sh, topk, info = build_layer(args.config, dev)
+    log(f"[bench] building workload config {cid}")
+    cfg, layer, x, st, sh, topk, info = build_layer(cid, dev)
     T = x.shape[0]
     b = layer.buffers(T, dev)
-    cap = T * cfg.k + T
     stream = torch.cuda.current_stream()
     ids_in, w_in = (topk if topk is not None else (None, None))
 
@@ -296,20 +298,20 @@ def main():
         layer.down(b)
         layer.combine(b, w_in)
 
-    log(f"[bench] warmup {args.warmup}")
+    log(f"[bench] c{cid}: warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] c{cid}: timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    tokens = T
-    value = tokens / (ms / 1e3)
+    value = T / (ms / 1e3)
     k_ms = float(np.mean([a.elapsed_time(z) for a, z in ev]))
+    log(f"[bench] c{cid}: {ms:.4f} ms/step, gate/up {k_ms:.4f} ms")
 
     graph_ms = None
     if args.graph:
@@ -406,6 +408,31 @@ def main():
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)
         line["graph_tokens_per_s"] = round(T / (graph_ms / 1e3), 2)
+    if with_cpu and args.cpu_sample > 0:
+        log(f"[bench] cpu oracle baseline on {args.cpu_sample} tokens")
+        line["cpu_baseline"] = cpu_baseline(cfg, layer, b, x, st, sh, topk, args.cpu_sample)
+    del layer, st, sh, b, x, hist, acc
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer runs on one "
+              "GPU's share and uses no collectives.", file=sys.stderr)
+        sys.exit(2)
+    import gc
+    import torch
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    line = measure(args.config, args, dev, with_cpu=True)
+    if args.decode_config and args.decode_config != args.config:
+        gc.collect()
+        torch.cuda.empty_cache()
+        d = measure(args.decode_config, args, dev, with_cpu=False)
+        line["decode"] = {key: d[key] for key in ("value", "unit", "ms_per_step", "dtype", "config",
+                                                  "roofline", "layer_roofline")}
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -414,9 +441,6 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
         del src, dst
-    if args.cpu_sample > 0:
-        log(f"[bench] cpu oracle baseline on {args.cpu_sample} tokens")
-        line["cpu_baseline"] = cpu_baseline(cfg, layer, b, x, st, sh, topk, args.cpu_sample)
     print(json.dumps(line), flush=True)
 
 

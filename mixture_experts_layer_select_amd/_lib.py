@@ -95,11 +95,30 @@ def _check(fn: str, status: int):
 
 
 def _ptr(t):
+    """Raw pointer of a tensor (or an int address). The library reads every
+    buffer as dense row-major memory, so a strided view is refused rather
+    than read as raw memory."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of shape {tuple(t.shape)} and strides {t.stride()} is not "
+                         "contiguous: the library reads dense row-major buffers")
     return t.data_ptr()
+
+
+def expect(t, name: str, dtypes, device=None):
+    """Check a tensor argument's dtype (one of `dtypes`), contiguity and
+    device before its pointer is handed to the library."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous (strides {t.stride()})")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
 
 
 def _stream(stream=None):

@@ -178,8 +178,27 @@ class MoELayer:
         L.moe_combine(b.y_perm, self.act_dt, b.slot_to_row, w, b.T, self.k, self.H, b.offsets,
                       self.E_local if self.shared is not None else -1, b.out, self.act_dt, stream)
 
+    def check_inputs(self, x: torch.Tensor, topk_ids=None, topk_w=None):
+        """x must be [T, H] in the layer's activation dtype on the weights'
+        device; given routing must be int32 ids and fp32 weights [T, k]."""
+        act = torch.float32 if self.fmt == "f32" else torch.bfloat16
+        dev = self.w13.device
+        L.expect(x, "x", (act,), dev)
+        if x.dim() != 2 or x.shape[1] != self.H:
+            raise ValueError(f"x: shape {tuple(x.shape)}, expected [T, {self.H}]")
+        if (topk_ids is None) != (topk_w is None):
+            raise ValueError("routing must be given as both topk_ids and topk_w, or neither")
+        if topk_ids is None and self.router is None:
+            raise ValueError("the layer has no router: pass topk_ids and topk_w")
+        for t, name, dt in ((topk_ids, "topk_ids", torch.int32), (topk_w, "topk_w", torch.float32)):
+            if t is not None:
+                L.expect(t, name, (dt,), dev)
+                if tuple(t.shape) != (x.shape[0], self.k):
+                    raise ValueError(f"{name}: shape {tuple(t.shape)}, expected [{x.shape[0]}, {self.k}]")
+
     def forward(self, x: torch.Tensor, topk_ids=None, topk_w=None, stream=None) -> LayerBuffers:
         """The whole layer. Routing comes from the router unless given."""
+        self.check_inputs(x, topk_ids, topk_w)
         b = self.buffers(x.shape[0], x.device)
         if topk_ids is None:
             self.route(x, b, stream)

@@ -58,3 +58,34 @@ def oracle_rows(x_rows, ids_rows, w_rows, st, shared, k, E_local, base, fmt, n_t
                            topk_w=np.asarray(w_rows), base=base, E_local=E_local,
                            fmt=oracle.FP8 if fmt == "fp8" else None, n_threads=n_threads)
     return res["out64"]
+
+
+def tile_cover_tokens(offsets, row_to_slot, T, k, n_groups, n_min, seed, tile=256):
+    """Tokens whose rows reach every m-tile of every group, filled up with
+    seeded random tokens to at least n_min.
+
+    A group of m rows is split into nt = ceil(m / tile) tiles of even height
+    (tile t holds rows [t*m/nt, (t+1)*m/nt)), as the grouped GEMMs split it;
+    one random row of every tile is taken, and its token is slot // k for a
+    routed slot, slot - T*k for a shared-group slot. Every output column of a
+    chosen token's rows is compared, so every n-block of every tile is
+    covered too."""
+    offsets = np.asarray(offsets)
+    row_to_slot = np.asarray(row_to_slot)
+    rng = np.random.default_rng(seed)
+    toks = set()
+    for g in range(n_groups):
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        m = b - a
+        if m <= 0:
+            continue
+        nt = (m + tile - 1) // tile
+        for t in range(nt):
+            lo, hi = a + t * m // nt, a + (t + 1) * m // nt
+            slot = int(row_to_slot[int(rng.integers(lo, hi))])
+            toks.add(slot // k if slot < T * k else slot - T * k)
+    rest = np.setdiff1d(np.arange(T), np.fromiter(toks, dtype=np.int64, count=len(toks)))
+    need = max(0, n_min - len(toks))
+    if need:
+        toks.update(int(t) for t in rng.choice(rest, min(need, len(rest)), replace=False))
+    return np.array(sorted(toks), dtype=np.int64)

@@ -187,3 +187,35 @@ def test_rebalance_device_calls_check_arguments(L):
     _expect(L, L.moe_count_accumulate, "MOE_ERR_INVALID_ARG", 1, -2, 1, 0)
     L.moe_coactivation(None, 0, 8, 16, None, 0)  # nothing to add: no device call
     L.moe_count_accumulate(None, 0, None, 0)
+
+
+def test_binding_refuses_strided_and_mistyped_tensors():
+    """A strided view or a wrong dtype is refused before any pointer reaches
+    the library (the library reads dense row-major buffers of the stated
+    dtype)."""
+    import torch
+    import mixture_experts_layer_select_amd as L
+    from mixture_experts_layer_select_amd import _lib
+    H, I, E, k = 256, 128, 4, 2
+    w13 = torch.zeros((E, 2 * I, H), dtype=torch.bfloat16)
+    w2 = torch.zeros((E, H, I), dtype=torch.bfloat16)
+    layer = L.MoELayer("bf16", H, I, k, w13, w2)
+    x = torch.zeros((5, H), dtype=torch.bfloat16)
+    ids = torch.zeros((5, k), dtype=torch.int32)
+    tw = torch.zeros((5, k), dtype=torch.float32)
+    layer.check_inputs(x, ids, tw)  # well-formed: no error
+    with pytest.raises(TypeError):
+        layer.check_inputs(x.float(), ids, tw)
+    with pytest.raises(ValueError):
+        layer.check_inputs(torch.zeros((H, 5), dtype=torch.bfloat16).t(), ids, tw)
+    with pytest.raises(TypeError):
+        layer.check_inputs(x, ids.long(), tw)
+    with pytest.raises(ValueError):
+        layer.check_inputs(x, ids, None)
+    with pytest.raises(ValueError):
+        layer.check_inputs(x, None, None)  # no router: routing must be given
+    with pytest.raises(ValueError):
+        layer.check_inputs(torch.zeros((5, H + 1), dtype=torch.bfloat16)[:, :H].contiguous()[:, :H - 1],
+                           ids, tw)
+    with pytest.raises(ValueError):
+        _lib._ptr(torch.zeros((4, 6))[:, ::2])

@@ -127,6 +127,30 @@ def test_ffn_fp8_r1_shape_large_group():
     _run("fp8", 7168, 2048, [300, 40], shared=False, seed=4)
 
 
+@pytest.mark.timeout(600)
+def test_ffn_fp8_r1_shape_large_group_all_panels():
+    """H=7168, I=2048, every row compared: a 2400-row expert is 10 even tiles
+    of 240 rows, run by the large-group launch in two full panels of 4 m-tiles
+    and a 2-tile remainder panel, with the full 56-step (gate/up) and 16-step
+    (down) K loops; a 513-row expert (3 tiles, one short panel), small
+    experts for the small-group launch, and a 300-row shared group (2
+    tiles)."""
+    _run("fp8", 7168, 2048, [2400, 0, 7, 513, 1, 120, 300], shared=True, seed=9)
+
+
+@pytest.mark.timeout(600)
+def test_ffn_bf16_r1_shape_wide_many_groups():
+    """H=7168, I=2048, every row compared: 120 routed experts of 0 to 6 rows
+    with three multi-tile ones among them (70, 150, 230 rows) and a 33-row
+    shared group. At most 32 rows per group over the buffer bound, so the
+    8-wave bf16 launch runs it (the decode shape's path)."""
+    rng = np.random.default_rng(21)
+    sizes = list(rng.integers(0, 7, 120))
+    sizes[7], sizes[60], sizes[111] = 70, 150, 230
+    assert sum(sizes) + 33 + 5 <= 32 * (len(sizes) + 1)
+    _run("bf16", 7168, 2048, sizes + [33], shared=True, seed=10)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
 def test_ffn_every_group_empty(fmt):
     """No group has a row: the launches find no work and write nothing."""

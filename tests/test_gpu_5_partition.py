@@ -41,6 +41,7 @@ def _counts(L, cfg, ids):
     return cnt[: cfg.E].cpu().to(torch.int64)
 
 
+@pytest.mark.timeout(600)
 def test_balanced_partition_flow_zipf13():
     import mixture_experts_layer_select_amd as L
     cfg = mi.CONFIGS[5]
@@ -104,11 +105,11 @@ def test_balanced_partition_flow_zipf13():
     assert np.array_equal(b.counts.cpu().numpy(), p["counts"])
     assert np.array_equal(b.row_to_slot.cpu().numpy(), p["row_to_slot"])
     local_tokens = np.nonzero(((got >= heavy * S) & (got < (heavy + 1) * S)).any(1))[0]
-    rows = np.sort(np.random.default_rng(5).choice(local_tokens, 8, replace=False))
+    rows = local_tokens  # every token with a pick in this set
     ref = oracle_rows(x[torch.from_numpy(rows).to(DEV)].cpu(), got[rows],
                       w_new.cpu().numpy()[rows], st, None, cfg.k, S, heavy * S, "bf16")
     e = rel_err(out_f64(b.out[torch.from_numpy(rows).to(DEV)]), ref)
-    say(f"  heaviest set sampled rel err {e:.3e}")
+    say(f"  heaviest set: all {len(rows)} local tokens compared, max rel err {e:.3e}")
     assert e <= 1e-2
     # tokens without a pick in this set get an exact zero row
     others = np.setdiff1d(np.arange(cfg.T), local_tokens)

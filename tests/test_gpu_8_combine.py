@@ -59,7 +59,9 @@ def test_combine_bf16_matches_oracle(T, k, H, shared):
     if not shared:
         empty = (s2r.reshape(T, k) < 0).all(axis=1)
         assert (got64[empty] == 0).all()
-    assert rel_err(got64, ref) <= 1e-2
+    # one fp32 sum of at most k + 1 terms, then one bf16 rounding (half an ulp
+    # is 2^-9 of the value): at most about 2e-3 of max|out|, with margin
+    assert rel_err(got64, ref) <= 4e-3
 
 
 @pytest.mark.parametrize("T,k,H", [(31, 8, 7168), (19, 4, 264), (13, 9, 7168)])
