@@ -182,6 +182,25 @@ moe_status moe_expert_ffn_down(const moe_expert_weights* w, const int32_t* exper
                                int n_groups, int max_rows, void* y_perm, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* moe_expert_ffn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the intermediate A (and its fp8 scales) lives in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends, instead of a caller workspace. Arguments, results and limits
+ * as for moe_expert_ffn; the call allocates and frees nothing.
+ *   Limit: moe_expert_ffn_workspace_size(w, max_rows) must not exceed
+ *   MOE_NOALLOC_SCRATCH_BYTES (else MOE_ERR_WORKSPACE and nothing is
+ *   enqueued); e.g. bf16 at I = 2048 allows 16384 rows, fp8 about 31700.
+ *   Calls that overlap on one GPU (other streams, other threads) share the
+ *   array and race: serialise them. Nothing in it needs clearing: every row
+ *   of A that the down projection reads is written by the gate/up step of
+ *   the same call. The first call on a device looks the array's address up
+ *   (hipGetSymbolAddress), so make one outside graph capture. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_expert_ffn_noalloc(const moe_expert_weights* w, const void* x_perm,
+                                  const float* x_perm_scale, const int32_t* expert_offsets,
+                                  int n_groups, int max_rows, void* y_perm, void* stream);
+
 /* fp8 gate/up without a permuted copy of the activations ([Moreh-EP] Library
  * optimization: the fused MoE kernel reads each expert's tokens itself):
  * moe_quantize_tokens quantises every token once, and

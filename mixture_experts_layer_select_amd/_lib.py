@@ -22,7 +22,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, 1, 2, 3, 4
 
 EXPORTS = [
     "moe_route", "moe_route_select_workspace_size", "moe_route_select", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
-    "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_quantize_tokens",
+    "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_expert_ffn_noalloc",
+    "moe_quantize_tokens",
     "moe_expert_ffn_gate_up_tokens", "moe_combine", "moe_balanced_partition", "moe_gather_rows",
     "moe_count_accumulate", "moe_coactivation", "moe_affinity_partition",
     "moe_status_string", "moe_last_error_message",
@@ -67,6 +68,7 @@ def lib() -> C.CDLL:
         L.moe_expert_ffn.argtypes = [C.POINTER(moe_expert_weights), p, p, p, i, i, p, p, sz, p]
         L.moe_expert_ffn_gate_up.argtypes = [C.POINTER(moe_expert_weights), p, p, p, i, i, p, sz, p]
         L.moe_expert_ffn_down.argtypes = [C.POINTER(moe_expert_weights), p, i, i, p, p, sz, p]
+        L.moe_expert_ffn_noalloc.argtypes = [C.POINTER(moe_expert_weights), p, p, p, i, i, p, p]
         L.moe_quantize_tokens.argtypes = [p, i, i, i, p, p, p]
         L.moe_expert_ffn_gate_up_tokens.argtypes = [C.POINTER(moe_expert_weights), p, p, i, i, p, p, i, i,
                                                     p, sz, p]
@@ -80,7 +82,7 @@ def lib() -> C.CDLL:
         L.moe_status_string.restype = C.c_char_p
         L.moe_last_error_message.restype = C.c_char_p
         for f in ("moe_route", "moe_route_select", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_gate_up",
-                  "moe_expert_ffn_down", "moe_quantize_tokens", "moe_expert_ffn_gate_up_tokens", "moe_combine",
+                  "moe_expert_ffn_down", "moe_expert_ffn_noalloc", "moe_quantize_tokens", "moe_expert_ffn_gate_up_tokens", "moe_combine",
                   "moe_balanced_partition", "moe_gather_rows", "moe_count_accumulate",
                   "moe_coactivation", "moe_affinity_partition"):
             getattr(L, f).restype = C.c_int
@@ -197,6 +199,17 @@ def moe_expert_ffn_gate_up(w: moe_expert_weights, x_perm, x_perm_scale, expert_o
     _check("moe_expert_ffn_gate_up", lib().moe_expert_ffn_gate_up(
         C.byref(w), _ptr(x_perm), _ptr(x_perm_scale), _ptr(expert_offsets), n_groups, max_rows,
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# size of the static device scratch behind moe_expert_ffn_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_expert_ffn_noalloc(w: moe_expert_weights, x_perm, x_perm_scale, expert_offsets, n_groups,
+                           max_rows, y_perm, stream=None):
+    _check("moe_expert_ffn_noalloc", lib().moe_expert_ffn_noalloc(
+        C.byref(w), _ptr(x_perm), _ptr(x_perm_scale), _ptr(expert_offsets), n_groups, max_rows,
+        _ptr(y_perm), _stream(stream)))
 
 
 def moe_quantize_tokens(x, x_dt, T, H, codes, scales, stream=None):

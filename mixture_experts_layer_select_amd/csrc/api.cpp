@@ -281,6 +281,33 @@ moe_status moe_expert_ffn(const moe_expert_weights* w, const void* x_perm, const
                            (hipStream_t)stream);
 }
 
+moe_status moe_expert_ffn_noalloc(const moe_expert_weights* w, const void* x_perm,
+                                  const float* x_perm_scale, const int32_t* expert_offsets,
+                                  int n_groups, int max_rows, void* y_perm, void* stream) {
+    g_msg[0] = 0;
+    moe_status s = check_weights(w);
+    if (s) return s;
+    REQUIRE(max_rows >= 0, MOE_ERR_INVALID_ARG, "moe_expert_ffn_noalloc: max_rows < 0");
+    const size_t need = ffn_workspace_bytes(w, max_rows);
+    REQUIRE(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+            "moe_expert_ffn_noalloc: max_rows=%d needs %zu bytes of scratch, the static array "
+            "holds %zu (use moe_expert_ffn with a workspace)",
+            max_rows, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void* scratch = nullptr;
+    if (max_rows > 0 && (s = ffn_noalloc_scratch(&scratch))) return s;
+    s = check_ffn_call("moe_expert_ffn_noalloc", w, n_groups, max_rows, expert_offsets, scratch,
+                       (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    if (s || max_rows == 0) return s;
+    REQUIRE(x_perm && y_perm, MOE_ERR_INVALID_ARG, "moe_expert_ffn_noalloc: null pointer");
+    REQUIRE(w->dt != MOE_FP8_E4M3 || x_perm_scale, MOE_ERR_INVALID_ARG,
+            "moe_expert_ffn_noalloc: fp8 needs x_perm_scale");
+    s = launch_ffn_gate_up(w, x_perm, x_perm_scale, expert_offsets, n_groups, max_rows, scratch,
+                           (hipStream_t)stream);
+    if (s) return s;
+    return launch_ffn_down(w, expert_offsets, n_groups, max_rows, y_perm, scratch,
+                           (hipStream_t)stream);
+}
+
 moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* slot_to_row,
                        const float* topk_w, int T, int k, int H, const int32_t* expert_offsets,
                        int shared_group, void* out, moe_dtype out_dt, void* stream) {

@@ -31,7 +31,9 @@
 // step; A and B use the same one, so the dot products are unchanged.
 #include "moe_internal.h"
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 namespace moe {
 namespace {
@@ -1193,6 +1195,34 @@ int persistent_grid_xcd(long bound, int per_cu) {
 
 size_t ffn_workspace_bytes(const moe_expert_weights* w, int max_rows) {
     return carve(w, max_rows, nullptr).bytes;
+}
+
+// Scratch of moe_expert_ffn_noalloc: the intermediate A (and its fp8 scales)
+// in a file-scope device array, so that entry point calls no allocator. Each
+// GPU holds its own copy for the life of the process. In host code the
+// array's name only stands in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+moe_status ffn_noalloc_scratch(void** ptr) {
+    static std::mutex mu;
+    static std::vector<void*> per_device;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)per_device.size() <= dev) per_device.resize(dev + 1, nullptr);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return set_error(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                             hipGetErrorString(e));
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return MOE_OK;
 }
 
 moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,

@@ -91,6 +91,9 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int base, int E_loca
                           void* x_perm, float* x_perm_scale, void* ws, hipStream_t st);
 
 size_t ffn_workspace_bytes(const moe_expert_weights* w, int max_rows);
+// device address of the static scratch of moe_expert_ffn_noalloc on the
+// current device (looked up on the first call per device)
+moe_status ffn_noalloc_scratch(void** ptr);
 // Where the fp8 gate/up GEMM reads permuted row r's activations: row r of
 // x_perm (row_slot null), or the row of its token in a [rows][H] token
 // buffer, token = slot < S ? slot / k : slot - S with slot = row_slot[r];

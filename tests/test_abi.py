@@ -219,3 +219,19 @@ def test_binding_refuses_strided_and_mistyped_tensors():
                            ids, tw)
     with pytest.raises(ValueError):
         _lib._ptr(torch.zeros((4, 6))[:, ::2])
+
+
+def test_noalloc_ffn_refuses_rows_beyond_its_static_scratch():
+    """moe_expert_ffn_noalloc checks the rows against its static scratch
+    before anything is enqueued (no device call is made here)."""
+    import torch
+    import mixture_experts_layer_select_amd as L
+    H, I, E = 512, 256, 2
+    w = L.make_weights(L.BF16, E, H, I, torch.zeros((E, 2 * I, H), dtype=torch.bfloat16),
+                       torch.zeros((E, H, I), dtype=torch.bfloat16))
+    big = L.NOALLOC_SCRATCH_BYTES // (I * 2) + 64
+    assert L.moe_expert_ffn_workspace_size(w, big) > L.NOALLOC_SCRATCH_BYTES
+    lib = L.lib()
+    st = lib.moe_expert_ffn_noalloc(C.byref(w), None, None, None, E, big, None, None)
+    assert lib.moe_status_string(st).decode() == "MOE_ERR_WORKSPACE"
+    assert b"static array" in lib.moe_last_error_message()
