@@ -77,7 +77,9 @@ moe_status moe_route(const void* x, const void* w_router, const float* bias, moe
 
 /* Gating for large token batches: the same topk_ids and topk_w as moe_route
  * (bit for bit), without computing every fixed-order logit. Approximate logits
- * and sum_h |x_h w_eh| come from bf16 MFMAs; a rigorous bound on the distance
+ * and sum_h |x_h w_eh| come from bf16 MFMAs over 64-deep stages added in fp32;
+ * a rigorous bound (valid for any internal MFMA summation order with 16 or
+ * more significant bits per addition, and for flushed denormals) on the distance
  * between an approximate logit and the fixed-order one leaves, per token, the
  * experts whose bound interval reaches the k-th largest lower bound. Only those
  * get their fixed-order logit (the selection rule of moe_route is then applied

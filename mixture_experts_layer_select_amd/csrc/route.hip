@@ -268,14 +268,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 // the k largest fixed-order logits is found from approximate logits and a
 // rigorous bound on their distance to the fixed-order ones:
 //   1. route_approx_kernel: a_e = sum_h x_h w_eh and s_e = sum_h |x_h| |w_eh|
-//      on bf16 MFMAs (bf16 products are exact in fp32).
+//      on bf16 MFMAs (bf16 products are exact in fp32 unless they underflow).
+//      Every 64-deep stage is summed by two chained MFMAs from zero; the stage
+//      results are added on the VALU in ascending K. It also writes max_h |w_eh| per expert
+//      and max_h |x_th| per token.
 //   2. route_refine_kernel, one wave per token: every bound below is taken in
-//      fp64 with a margin. Whatever the MFMA's internal summation order, with
-//      fp32-or-better intermediates and at most 2 units of fp32 rounding per
-//      step (u = 2^-22: twice truncation), |a_e - S_e| <= g(n) s_e/(1 - g(n))
-//      with n = H + 64 additions (the K tail of the last stage is zeros)
-//      (S_e the exact dot product, g(n) = n u/(1 - n u)), plus H * 2^-126 for
-//      flushed tiny products. The fixed-order value c_e differs from S_e by at
+//      fp64 with a margin. The MFMA part of the error only depends on a
+//      64-term sum being within gamma(64, 2^-16) of exact relative to the sum
+//      of magnitudes (16 significant bits per addition in any order or
+//      alignment; fp32 arithmetic has 24), the chunk sums on IEEE fp32 adds,
+//      and flushed tiny values (a denormal input, product or partial) costing
+//      at most 2^-126 (1 + |w| + |x|) per product and 2^-126 per addition;
+//      max |x| of the token and max |w| of the expert bound the latter. The
+//      fixed-order value c_e differs from S_e (the exact dot product) by at
 //      most g'(8 ceil(H/512) + 6) s_e (round to nearest, 2^-24: each lane's
 //      partial adds 8 ceil(H/512) products, the tree adds 6 levels). The
 //      bias add rounds both once. With D_e bounding |approx_e - logit_e|,
@@ -319,7 +324,9 @@ struct ApproxStage {
 __global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w, int T,
                                                            int H, int E, float* __restrict__ approx,
-                                                           float* __restrict__ sabs) {
+                                                           float* __restrict__ sabs,
+                                                           float* __restrict__ wmax,
+                                                           float* __restrict__ xmax) {
     __shared__ __attribute__((aligned(1024))) ApproxStage st[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -366,6 +373,13 @@ __global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __res
             }
         }
     };
+    // the first token tile's workgroups also take max |w| of each expert row,
+    // the first expert tile's max |x| of each token row (bf16 magnitudes
+    // compare as integers once the sign bit is cleared)
+    const bool row_max = blockIdx.x == 0;
+    const bool tok_max = blockIdx.y == 0;
+    uint32_t wm_bits[2] = {0u, 0u};
+    uint32_t xm_bits[2] = {0u, 0u};
     auto store = [&](int slot, ApproxStage& S) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -374,6 +388,20 @@ __global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __res
             const int o = r * kApproxK + ((c ^ ((r >> 1) & 7)) << 3);
             *reinterpret_cast<u32x4*>(&S.x[o]) = rx[slot][i];
             *reinterpret_cast<u32x4*>(&S.w[o]) = rw[slot][i];
+            if (row_max) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t u = rw[slot][i][v];
+                    wm_bits[i] = max(wm_bits[i], max(u & 0x7fffu, (u >> 16) & 0x7fffu));
+                }
+            }
+            if (tok_max) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t u = rx[slot][i][v];
+                    xm_bits[i] = max(xm_bits[i], max(u & 0x7fffu, (u >> 16) & 0x7fffu));
+                }
+            }
         }
     };
     f32x4 acc[4][2], aab[4][2];
@@ -388,7 +416,12 @@ __global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __res
         const int c = 4 * sub + lk;
         return *reinterpret_cast<const u32x4*>(&base[row * kApproxK + ((c ^ ((row >> 1) & 7)) << 3)]);
     };
+    // Each stage (64 deep) is one chain of two MFMAs from zero, added to its
+    // sum on the VALU, stage after stage in ascending K: an MFMA only ever
+    // sums exact products of one stage, whatever its internal order.
     auto compute = [&](const ApproxStage& S) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 ta[4][2], tb[4][2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             u32x4 fa[4], fb[2], ga[4], gb[2];
@@ -406,10 +439,17 @@ __global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __res
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-                    aab[i][j] = mfma16x16x32(ga[i], gb[j], aab[i][j]);
+                    ta[i][j] = mfma16x16x32(fa[i], fb[j], sub ? ta[i][j] : z);
+                    tb[i][j] = mfma16x16x32(ga[i], gb[j], sub ? tb[i][j] : z);
                 }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                acc[i][j] += ta[i][j];
+                aab[i][j] += tb[i][j];
+            }
     };
     // step s (u = s mod 6 fixes the register slot and the LDS buffer):
     // compute stage s from LDS buffer s%2, store stage s+1 from its register
@@ -441,6 +481,29 @@ __global__ __launch_bounds__(512) void route_approx_kernel(const uint16_t* __res
         step(sidx + 5, std::integral_constant<int, 5>{});
         if (sidx + 6 >= nst) break;
     }
+    if (row_max) {
+        // the 8 threads of a row are 8 consecutive lanes
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t m = wm_bits[i];
+            m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+            const int r = (tid + 512 * i) >> 3;
+            if ((tid & 7) == 0 && e0 + r < E) wmax[e0 + r] = __uint_as_float(m << 16);
+        }
+    }
+    if (tok_max) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t m = xm_bits[i];
+            m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+            const int r = (tid + 512 * i) >> 3;
+            if ((tid & 7) == 0 && t0 + r < T) xmax[t0 + r] = __uint_as_float(m << 16);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -468,12 +531,31 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __res
                                                            const float* __restrict__ bias, int T,
                                                            int H, int E, int k,
                                                            float* __restrict__ logits,
-                                                           const float* __restrict__ sabs) {
+                                                           const float* __restrict__ sabs,
+                                                           const float* __restrict__ wmax,
+                                                           const float* __restrict__ xmax,
+                                                           int32_t* __restrict__ ncand) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const int nsteps = (H + 511) / 512;  // steps with data; the rest read zeros
-    const double gm = gamma_n((double)H + 64.0, 0x1p-22);  // zero-padded K tail included
+    const double mx = (double)xmax[t];  // max |x| of the token
+    // Distance of the approximate sums from the exact dot product S = sum x w,
+    // with A = sum |x w| (the same bound for every internal MFMA order):
+    //  - each stage's sum (two chained 32-deep MFMAs from zero: 64 products
+    //    and at most 64 additions) is within gamma(64, 2^-16) * A_stage of its
+    //    exact sum: at least 16 significant bits per addition, in any order or
+    //    operand alignment (fp32 keeps 24);
+    //  - the nc = ceil(H/64) stage sums are added on the VALU in IEEE fp32
+    //    (gamma(nc, 2^-24)), the signed sums and the absolute sums alike;
+    //  - flushes: a tiny product, a tiny chunk result, or a tiny (denormal)
+    //    input x_h or w_h dropped by the MFMA loses at most 2^-126 (1 + |w_h|
+    //    + |x_h|) per product plus 2^-126 per addition: F below.
+    // The absolute sums give A <= (s_a + 2F) / (1 - g). The fixed-order logit
+    // is within gamma(8 ceil(H/512) + 6, 2^-24) A of S (fma chains per lane,
+    // then the 6-level tree), plus F should the VALU flush as well.
+    const double nc = (double)((H + 63) / 64);
+    const double g = gamma_n(64.0, 0x1p-16) + 2.0 * gamma_n(nc, 0x1p-24);
     const double gc = gamma_n(8.0 * nsteps + 6.0, 0x1p-24);
     // bounds of every expert's logit, rounded outward to fp32
     float lo[4], hi[4];
@@ -486,8 +568,9 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __res
             const double a = logits[(size_t)t * E + e];
             const double sa = sabs[(size_t)t * E + e];
             const double b = bias ? (double)bias[e] : 0.0;
-            const double s_true = sa / (1.0 - gm) + (double)H * 0x1p-126;  // >= sum |x w|
-            const double d_sum = gm * s_true + gc * s_true + (double)H * 0x1p-126;
+            const double F = 0x1p-126 * ((double)H * (1.0 + (double)wmax[e] + mx) + 64.0 * nc + 64.0);
+            const double a_up = (sa + 2.0 * F) / (1.0 - g);  // >= sum |x w|
+            const double d_sum = (g + gc) * a_up + 3.0 * F;
             const double v = a + b;
             // both sides round once more when the bias is added
             const double d = (d_sum + (fabs(v) + d_sum) * 0x1p-23) * (1.0 + 0x1p-20) + 0x1p-100;
@@ -513,6 +596,14 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __res
         kth = best;
     }
     const float L = from_ordered((uint32_t)(kth >> 32));
+    // the candidates: experts whose upper bound reaches L (wave-uniform masks)
+    uint64_t cmask[4];
+    int n_cand = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        cmask[i] = __ballot(lane + 64 * i < E && hi[i] >= L);
+        n_cand += __builtin_popcountll(cmask[i]);
+    }
     // this token's row of x, one 8-element chunk per lane and step. Rows are
     // read through a descriptor of the row's size: chunks past H read zeros,
     // whose products add exact zeros to a partial (which is never -0), so all
@@ -524,7 +615,7 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e_lane = lane + 64 * i;
-        uint64_t cand = __ballot(e_lane < E && hi[i] >= L);
+        uint64_t cand = cmask[i];
         float mine = -__builtin_inff();
         // one candidate at a time; the next candidate's row is loaded while
         // the current one is summed (after the last, the same row again, so
@@ -574,6 +665,7 @@ __global__ __launch_bounds__(256) void route_refine_kernel(const uint16_t* __res
         }
         if (e_lane < E) logits[(size_t)t * E + e_lane] = mine;
     }
+    if (lane == 0) ncand[t] = n_cand;
 }
 
 }  // namespace
@@ -599,18 +691,26 @@ moe_status launch_route(const void* x, const void* w, const float* bias, moe_dty
 
 namespace moe {
 
+// workspace: approximate sums [T][E] | absolute sums [T][E] | max |w| per
+// expert [E] | max |x| per token [T] | candidates per token [T] (int32, a
+// diagnostic)
 size_t route_select_workspace_bytes(int T, int E) {
-    return 2 * align_up((size_t)T * E * sizeof(float), 256);
+    return 2 * align_up((size_t)T * E * sizeof(float), 256) + align_up((size_t)E * sizeof(float), 256) +
+           2 * align_up((size_t)T * sizeof(int32_t), 256);
 }
 
 moe_status launch_route_select(const void* x, const void* w, const float* bias, int T, int H, int E,
                                int k, int scoring, int renorm, int32_t* ids, float* topk_w, void* ws,
                                hipStream_t st) {
+    const size_t te = align_up((size_t)T * E * sizeof(float), 256);
     float* approx = (float*)ws;
-    float* sabs = (float*)((uint8_t*)ws + align_up((size_t)T * E * sizeof(float), 256));
+    float* sabs = (float*)((uint8_t*)ws + te);
+    float* wmax = (float*)((uint8_t*)ws + 2 * te);
+    float* xmax = (float*)((uint8_t*)ws + 2 * te + align_up((size_t)E * sizeof(float), 256));
+    int32_t* ncand = (int32_t*)((uint8_t*)xmax + align_up((size_t)T * sizeof(float), 256));
     hipLaunchKernelGGL(route_approx_kernel,
                        dim3((T + kApproxT - 1) / kApproxT, (E + kApproxE - 1) / kApproxE), dim3(512), 0, st,
-                       (const uint16_t*)x, (const uint16_t*)w, T, H, E, approx, sabs);
+                       (const uint16_t*)x, (const uint16_t*)w, T, H, E, approx, sabs, wmax, xmax);
     moe_status s = check_launch("route_approx_kernel");
     if (s != MOE_OK) return s;
     // the smallest register-resident row that holds H (H <= 8192)
@@ -619,7 +719,7 @@ moe_status launch_route_select(const void* x, const void* w, const float* bias, 
                 : nsteps <= 8 ? route_refine_kernel<8>
                 : nsteps <= 14 ? route_refine_kernel<14> : route_refine_kernel<16>;
     hipLaunchKernelGGL(refine, dim3((T + 3) / 4), dim3(256), 0, st, (const uint16_t*)x,
-                       (const uint16_t*)w, bias, T, H, E, k, approx, sabs);
+                       (const uint16_t*)w, bias, T, H, E, k, approx, sabs, wmax, xmax, ncand);
     s = check_launch("route_refine_kernel");
     if (s != MOE_OK) return s;
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, approx, T, E, k, scoring,

@@ -127,3 +127,29 @@ def test_route_select_rejects_what_it_does_not_cover():
             L.moe_route_select(x, wr, None, a["dt"], 8, a["H"], 32, 4, a["scoring"], a["renorm"], ids, w,
                                ws, a["ws_bytes"])
         assert e.value.status == status
+
+
+def test_route_select_denormal_inputs_and_large_weights():
+    """Denormal bf16 activations and weights next to router rows scaled up to
+    |w| of about 20: the bound covers a flushed tiny input times a large
+    weight, so the selection still matches moe_route (and the oracle's ids)
+    bit for bit, with close logit races among the scaled rows."""
+    T, H, E, k = 600, 1024, 64, 6
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    x = torch.randn((T, H), generator=g, device=DEV)
+    wr = torch.randn((E, H), generator=g, device=DEV) * 0.006
+    # a tenth of the activations become bf16 denormals (+-1..127 x 2^-133)
+    tiny = torch.randint(1, 128, (T, H), generator=g, device=DEV).float() * 2.0 ** -133
+    sign = torch.where(torch.rand((T, H), generator=g, device=DEV) < 0.5, -1.0, 1.0)
+    mask = torch.rand((T, H), generator=g, device=DEV) < 0.1
+    x = torch.where(mask, tiny * sign, x).to(torch.bfloat16)
+    # eight experts with large weights (|w| up to ~20), a few denormal weights
+    wr[::8] *= 1000.0
+    wmask = torch.rand((E, H), generator=g, device=DEV) < 0.05
+    wr = torch.where(wmask, torch.full_like(wr, 3.0 * 2.0 ** -130), wr).to(torch.bfloat16)
+    xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert ((xb & 0x7f80) == 0).sum() > T * H // 20  # denormals really are there
+    si, sw = _same_as_route(x, wr, None, k, oracle.SIGMOID, True)
+    _, oi, _ = oracle.route(x.cpu(), wr.cpu(), None, k, oracle.SIGMOID, True)
+    assert np.array_equal(si, oi)
