@@ -140,7 +140,10 @@ def build_partition_layer(cfg, dev):
     g_before = ev_before.view(G, S).sum(1)
     g_after = ev_after.view(G, S).sum(1)
     heavy = int(torch.argmax(g_after).item())
-    heavy_before = int(torch.argmax(g_before).item())
+    # a larger held-out batch: the set loads without the sampling noise of 512 tokens
+    xh = mi.tokens(cfg, T=4096, device=dev, tensor=mi.XHELD)
+    h_before = counts_of(xh, wr, bias)[0].view(G, S).sum(1)
+    h_after = counts_of(xh, wr2, b2)[0].view(G, S).sum(1)
     old_ids = n2o[heavy * S:(heavy + 1) * S].tolist()
     st = mi.stacked_expert_weights(cfg, old_ids, device=dev)
     layer = L.MoELayer(cfg.fmt, cfg.H, cfg.I, cfg.k, st["w13"], st["w2"], shared=None, router=None,
@@ -150,6 +153,8 @@ def build_partition_layer(cfg, dev):
         calib_max_over_mean_balanced=round(loads.max().item() / mean, 4),
         eval_max_over_mean_contiguous=round(g_before.max().item() / (ev_before.sum().item() / G), 4),
         eval_max_over_mean_balanced=round(g_after.max().item() / (ev_after.sum().item() / G), 4),
+        heldout4096_max_over_mean_contiguous=round(h_before.max().item() / (h_before.sum().item() / G), 4),
+        heldout4096_max_over_mean_balanced=round(h_after.max().item() / (h_after.sum().item() / G), 4),
         heaviest_group=heavy, heaviest_group_rows=int(g_after.max().item()),
         heaviest_group_rows_contiguous=int(g_before.max().item()),
         heaviest_group_hit_experts=int((ev_after.view(G, S)[heavy] > 0).sum().item()),

@@ -34,7 +34,7 @@ from typing import Optional
 import torch
 
 # tensor ids used in seeds
-X, WR, RANK, W13, W2, WS13, WS2, ROUTING, XCAL = 1, 2, 3, 4, 5, 6, 7, 8, 9
+X, WR, RANK, W13, W2, WS13, WS2, ROUTING, XCAL, XHELD = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 
 BLOCK = 128          # fp8 block edge (weights 128x128, activations 1x128)
 E4M3_MAX = 448.0     # largest finite OCP e4m3fn value

@@ -95,6 +95,19 @@ def test_balanced_partition_flow_zipf13():
     say(f"  eval max/mean: contiguous {ev_old.max() / ev_old.mean():.3f}, "
         f"balanced {ev.max() / ev.mean():.3f}; heaviest set {heavy} with {ev[heavy]} rows")
 
+    # a larger held-out batch separates the partition's quality from the
+    # sampling noise of 512 tokens (a set's load varies by a few percent there)
+    xh = mi.tokens(cfg, T=4096, device=DEV, tensor=mi.XHELD)
+    ids_h, _ = _route(L, cfg, xh, wr2, b2)
+    ids_h_old, _ = _route(L, cfg, xh, wr, bias)
+    torch.cuda.synchronize()
+    hv = np.bincount(ids_h.cpu().numpy().ravel(), minlength=cfg.E).reshape(G, S).sum(1)
+    hv_old = np.bincount(ids_h_old.cpu().numpy().ravel(), minlength=cfg.E).reshape(G, S).sum(1)
+    say(f"  held-out 4096 tokens max/mean: contiguous {hv_old.max() / hv_old.mean():.3f}, "
+        f"balanced {hv.max() / hv.mean():.3f}")
+    assert hv_old.max() / hv_old.mean() > 1.3
+    assert hv.max() / hv.mean() < 1.05  # "within 5%" on a batch large enough to see it
+
     # one GPU's share: the heaviest set's 32 experts, in the new order
     old_ids = n2o[heavy * S:(heavy + 1) * S].tolist()
     st = mi.stacked_expert_weights(cfg, old_ids, device=DEV)
