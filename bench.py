@@ -56,6 +56,9 @@ def parse():
                     help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--fused-T", default="1,16,64,256",
+                    help="batch sizes at which the one-launch layer (moe_layer_fused) is timed against "
+                         "the five-launch path on the same weights ('' = skip)")
     ap.add_argument("--graph", action="store_true",
                     help="after the eager timed steps, capture one step in a HIP graph and also "
                          "report the replay time (graph_ms_per_step)")
@@ -274,6 +277,50 @@ def cpu_baseline(cfg, layer, b, x, st, sh, topk, n_sample):
                       f"scaled per token"}
 
 
+def fused_sweep(cfg, layer, Ts, dev, reps=50, warm=5):
+    """The layer at small batches: the five-launch path (route, permute, gate/up,
+    down, combine) eagerly and replayed from a HIP graph, and the one-launch
+    layer, on the same weights and tokens; mean ms per call from HIP events on
+    the launch stream."""
+    import torch
+    import moe_inputs as mi
+    stream = torch.cuda.current_stream()
+    res = {}
+    for T in Ts:
+        if T > layer.FUSED_MAX_T:
+            continue
+        x = mi.tokens(cfg, T=T, device=dev, tensor=20)
+
+        def timed(fn):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        sep = timed(lambda: layer.forward(x))
+        fused = timed(lambda: layer.forward_fused(x))
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                layer.forward(x)
+        stream.wait_stream(side)
+        graph = timed(g.replay)
+        err = int(layer.fused_workspace(T)[8:12].view(torch.int32).item())
+        res[str(T)] = {"five_launch_ms": round(sep, 4), "five_launch_graph_ms": round(graph, 4),
+                       "fused_ms": round(fused, 4), "fused_barrier_error": err}
+        log(f"[bench] T={T}: five launches {sep:.4f} ms (graph {graph:.4f}), one launch {fused:.4f} ms")
+        del g
+    return res
+
+
 def measure(cid: int, args, dev: str, with_cpu: bool) -> dict:
     """Time one workload (warm-up, then args.steps whole-layer steps) and
     return its JSON fields."""
@@ -410,6 +457,10 @@ def measure(cid: int, args, dev: str, with_cpu: bool) -> dict:
                       "affinity_partition_host_ms": round(part_ms, 3),
                       "partition": f"E={cfg.E} into {G} sets, load cap +2%"},
     }
+    Ts = [int(t) for t in args.fused_T.split(",") if t.strip()]
+    if Ts and layer.router is not None and layer.E_local == cfg.E and cfg.k <= 8:
+        line["fused_small_batch"] = {"layer": f"c{cfg.cid} weights, {cfg.fmt}",
+                                     **fused_sweep(cfg, layer, Ts, dev)}
     if graph_ms is not None:
         line["graph_ms_per_step"] = round(graph_ms, 4)
         line["graph_tokens_per_s"] = round(T / (graph_ms / 1e3), 2)
@@ -437,7 +488,8 @@ def main():
         torch.cuda.empty_cache()
         d = measure(args.decode_config, args, dev, with_cpu=False)
         line["decode"] = {key: d[key] for key in ("value", "unit", "ms_per_step", "dtype", "config",
-                                                  "roofline", "layer_roofline")}
+                                                  "roofline", "layer_roofline", "fused_small_batch")
+                          if key in d}
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -229,6 +229,35 @@ moe_status moe_expert_ffn_gate_up_tokens(const moe_expert_weights* w, const void
                                          int n_groups, int max_rows, void* workspace,
                                          size_t ws_bytes, void* stream);
 
+/* The whole layer for a small batch in one persistent launch ([Moreh-EP]
+ * Library optimization: a fused MoE kernel for small batches; Use of HIP
+ * Graphs: static sizes, capturable): the gating of moe_route, the permutation
+ * of moe_permute (all E experts local, the shared expert as group E when the
+ * weights hold one), the expert FFN of moe_expert_ffn (fp8: activations
+ * quantised per token and read through the permutation, as
+ * moe_quantize_tokens + moe_expert_ffn_gate_up_tokens) and moe_combine, as
+ * phases of one kernel separated by grid-wide barriers. Results are bit for
+ * bit those of the separate calls on the same inputs.
+ *   x [T,H] bf16, w_router [E,H] bf16, bias [E] fp32 or NULL, w: E_local == E
+ *   experts in bf16 or fp8 (+ optional shared expert); topk_ids [T,k] int32,
+ *   topk_w [T,k] fp32 and out [T,H] bf16 (out).
+ *   workspace: moe_layer_fused_workspace_size(w, T, E, k) bytes of device
+ *   memory; its first 256 bytes (the barrier words) must be zero before the
+ *   first call, and every completed call leaves them zero. The other contents
+ *   on return are unspecified.
+ * Limits: 1 <= T <= 256, 1 <= k <= 8, k <= E <= 256, H % 256 == 0,
+ * I % 128 == 0 (fp8: H, I <= 16384). The grid is one workgroup per CU and
+ * its phases wait for each other: the device must hold the whole grid at
+ * once (nothing else running on it). A barrier that waits too long (about
+ * a second) sets the third 32-bit workspace word (bytes 8..11) nonzero and lets the
+ * kernel finish; its outputs are then invalid and the first 256 bytes must
+ * be zeroed again. */
+size_t moe_layer_fused_workspace_size(const moe_expert_weights* w, int T, int E, int k);
+moe_status moe_layer_fused(const void* x, const void* w_router, const float* bias, int T, int E,
+                           int k, moe_scoring scoring, int renormalize,
+                           const moe_expert_weights* w, int32_t* topk_ids, float* topk_w,
+                           void* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Routing-weighted combine back to token order ([Moreh-EP] Overview:
  * dispatch/combine; the local half of it).
  *   out[t] = sum_{j: slot_to_row[t*k+j] >= 0} topk_w[t,j] * y_perm[slot_to_row[t*k+j]]

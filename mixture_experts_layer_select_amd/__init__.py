@@ -11,7 +11,8 @@ from ._lib import (BF16, F32, FP8_E4M3, SIGMOID, SOFTMAX, EXPORTS, MoEError, lib
                    moe_combine, moe_count_accumulate, moe_expert_ffn, moe_expert_ffn_down,
                    moe_expert_ffn_gate_up, moe_expert_ffn_gate_up_tokens, moe_expert_ffn_noalloc,
                    NOALLOC_SCRATCH_BYTES,
-                   moe_expert_ffn_workspace_size, moe_gather_rows, moe_permute,
+                   moe_expert_ffn_workspace_size, moe_gather_rows, moe_layer_fused,
+                   moe_layer_fused_workspace_size, moe_permute,
                    moe_permute_workspace_size, moe_quantize_tokens, moe_route, moe_route_select,
                    moe_route_select_workspace_size)
 from .layer import LayerBuffers, MoELayer

@@ -24,7 +24,8 @@ EXPORTS = [
     "moe_route", "moe_route_select_workspace_size", "moe_route_select", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
     "moe_expert_ffn", "moe_expert_ffn_gate_up", "moe_expert_ffn_down", "moe_expert_ffn_noalloc",
     "moe_quantize_tokens",
-    "moe_expert_ffn_gate_up_tokens", "moe_combine", "moe_balanced_partition", "moe_gather_rows",
+    "moe_expert_ffn_gate_up_tokens", "moe_layer_fused_workspace_size", "moe_layer_fused", "moe_combine",
+    "moe_balanced_partition", "moe_gather_rows",
     "moe_count_accumulate", "moe_coactivation", "moe_affinity_partition",
     "moe_status_string", "moe_last_error_message",
 ]
@@ -72,6 +73,10 @@ def lib() -> C.CDLL:
         L.moe_quantize_tokens.argtypes = [p, i, i, i, p, p, p]
         L.moe_expert_ffn_gate_up_tokens.argtypes = [C.POINTER(moe_expert_weights), p, p, i, i, p, p, i, i,
                                                     p, sz, p]
+        L.moe_layer_fused_workspace_size.argtypes = [C.POINTER(moe_expert_weights), i, i, i]
+        L.moe_layer_fused_workspace_size.restype = sz
+        L.moe_layer_fused.argtypes = [p, p, p, i, i, i, i, i, C.POINTER(moe_expert_weights), p, p, p, p,
+                                      sz, p]
         L.moe_combine.argtypes = [p, i, p, p, i, i, i, p, i, p, i, p]
         L.moe_balanced_partition.argtypes = [p, i, i, p, p, p]
         L.moe_gather_rows.argtypes = [p, i, p, p, i, sz, p]
@@ -82,7 +87,8 @@ def lib() -> C.CDLL:
         L.moe_status_string.restype = C.c_char_p
         L.moe_last_error_message.restype = C.c_char_p
         for f in ("moe_route", "moe_route_select", "moe_permute", "moe_expert_ffn", "moe_expert_ffn_gate_up",
-                  "moe_expert_ffn_down", "moe_expert_ffn_noalloc", "moe_quantize_tokens", "moe_expert_ffn_gate_up_tokens", "moe_combine",
+                  "moe_expert_ffn_down", "moe_expert_ffn_noalloc", "moe_quantize_tokens", "moe_expert_ffn_gate_up_tokens",
+                  "moe_layer_fused", "moe_combine",
                   "moe_balanced_partition", "moe_gather_rows", "moe_count_accumulate",
                   "moe_coactivation", "moe_affinity_partition"):
             getattr(L, f).restype = C.c_int
@@ -222,6 +228,17 @@ def moe_expert_ffn_gate_up_tokens(w: moe_expert_weights, x_tokens, x_tokens_scal
     _check("moe_expert_ffn_gate_up_tokens", lib().moe_expert_ffn_gate_up_tokens(
         C.byref(w), _ptr(x_tokens), _ptr(x_tokens_scale), T, k, _ptr(row_to_slot),
         _ptr(expert_offsets), n_groups, max_rows, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_layer_fused_workspace_size(w: moe_expert_weights, T, E, k) -> int:
+    return int(lib().moe_layer_fused_workspace_size(C.byref(w), T, E, k))
+
+
+def moe_layer_fused(x, w_router, bias, T, E, k, scoring, renormalize, w: moe_expert_weights, topk_ids,
+                    topk_w, out, workspace, ws_bytes, stream=None):
+    _check("moe_layer_fused", lib().moe_layer_fused(
+        _ptr(x), _ptr(w_router), _ptr(bias), T, E, k, scoring, int(bool(renormalize)), C.byref(w),
+        _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def moe_expert_ffn_down(w: moe_expert_weights, expert_offsets, n_groups, max_rows, y_perm, workspace,

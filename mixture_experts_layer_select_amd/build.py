@@ -23,7 +23,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["api.cpp", "partition.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "rebalance.hip"]
+SOURCES = ["api.cpp", "partition.cpp", "route.hip", "permute.hip", "ffn.hip", "combine.hip", "rebalance.hip",
+           "fused.hip"]
 
 
 def _compile(src: str, verbose: bool, extra=(), build_dir=BUILD) -> str:

@@ -308,6 +308,43 @@ moe_status moe_expert_ffn_noalloc(const moe_expert_weights* w, const void* x_per
                            (hipStream_t)stream);
 }
 
+size_t moe_layer_fused_workspace_size(const moe_expert_weights* w, int T, int E, int k) {
+    if (T < 0 || E < 1 || k < 1 || check_weights(w) != MOE_OK) return 0;
+    return layer_fused_workspace_bytes(w, T, E, k);
+}
+
+moe_status moe_layer_fused(const void* x, const void* w_router, const float* bias, int T, int E,
+                           int k, moe_scoring scoring, int renormalize,
+                           const moe_expert_weights* w, int32_t* topk_ids, float* topk_w,
+                           void* out, void* workspace, size_t ws_bytes, void* stream) {
+    g_msg[0] = 0;
+    moe_status s = check_weights(w);
+    if (s) return s;
+    REQUIRE(T >= 0 && E >= 1 && k >= 1 && k <= E, MOE_ERR_INVALID_ARG,
+            "moe_layer_fused: need T >= 0, 1 <= k <= E (T=%d E=%d k=%d)", T, E, k);
+    REQUIRE(scoring == MOE_SOFTMAX || scoring == MOE_SIGMOID, MOE_ERR_INVALID_ARG,
+            "moe_layer_fused: unknown scoring %d", (int)scoring);
+    REQUIRE(T <= 256 && k <= 8 && E <= 256, MOE_ERR_UNSUPPORTED,
+            "moe_layer_fused: needs T <= 256, k <= 8, E <= 256 (T=%d k=%d E=%d)", T, k, E);
+    REQUIRE(w->E_local == E, MOE_ERR_INVALID_ARG,
+            "moe_layer_fused: all experts must be local (E_local=%d, E=%d)", w->E_local, E);
+    REQUIRE(w->dt == MOE_BF16 || w->dt == MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED,
+            "moe_layer_fused: bf16 or fp8 experts");
+    REQUIRE(w->H % 256 == 0 && w->I % 128 == 0, MOE_ERR_UNSUPPORTED,
+            "moe_layer_fused: needs H %% 256 == 0 and I %% 128 == 0 (H=%d I=%d)", w->H, w->I);
+    REQUIRE(!w->ws13 == !w->ws2, MOE_ERR_INVALID_ARG, "moe_layer_fused: shared w13 without w2 or back");
+    REQUIRE(w->dt != MOE_FP8_E4M3 || !w->ws13 || (w->ws13_scale && w->ws2_scale), MOE_ERR_INVALID_ARG,
+            "moe_layer_fused: fp8 shared expert needs scales");
+    if (T == 0) return MOE_OK;
+    REQUIRE(x && w_router && topk_ids && topk_w && out, MOE_ERR_INVALID_ARG,
+            "moe_layer_fused: null pointer");
+    const size_t need = layer_fused_workspace_bytes(w, T, E, k);
+    REQUIRE(workspace && ws_bytes >= need, MOE_ERR_WORKSPACE, "moe_layer_fused: workspace %zu < %zu bytes",
+            ws_bytes, need);
+    return launch_layer_fused(x, w_router, bias, T, E, k, scoring, renormalize ? 1 : 0, w, topk_ids,
+                              topk_w, out, workspace, (hipStream_t)stream);
+}
+
 moe_status moe_combine(const void* y_perm, moe_dtype y_dt, const int32_t* slot_to_row,
                        const float* topk_w, int T, int k, int H, const int32_t* expert_offsets,
                        int shared_group, void* out, moe_dtype out_dt, void* stream) {

@@ -106,6 +106,10 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                               const float* x_perm_scale, const int32_t* offsets, int n_groups,
                               int max_rows, void* ws, hipStream_t st,
                               const ActSrc& src = ActSrc{nullptr, 0, 0, 0, 0});
+size_t layer_fused_workspace_bytes(const moe_expert_weights* w, int T, int E, int k);
+moe_status launch_layer_fused(const void* x, const void* w_router, const float* bias, int T, int E, int k,
+                              int scoring, int renorm, const moe_expert_weights* w, int32_t* topk_ids,
+                              float* topk_w, void* out, void* ws, hipStream_t st);
 moe_status launch_quantize_tokens(const void* x, int T, int H, void* codes, float* scales,
                                   hipStream_t st);
 moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, int n_groups,

@@ -14,13 +14,12 @@
 //            of the bits below it, so rows come out in (expert, slot) order
 //   fill     rows past the routed ones: shared-expert rows, then -1
 //   gather   x_perm[row] = x[token(row)] (bit copy or 1x128 e4m3 quantisation)
-#include "moe_internal.h"
+#include "permute_dev.h"
 
 namespace moe {
 namespace {
 
 constexpr int kChunk = 1024;   // slots per chunk
-constexpr int kMaxLocal = 256; // local experts handled per launch
 
 __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, long S,
                                                         int base, int E_local,
@@ -268,50 +267,6 @@ __global__ __launch_bounds__(256) void perm_gather_copy_kernel(
     }
 }
 
-// bf16 rows -> e4m3 codes + one fp32 scale per 128 elements; H % 128 == 0.
-// 16 lanes own one 128-element block, 8 elements each; a pass of four rounds
-// issues all of its row loads before the first block is quantised. Scales are
-// K-major: block b of row r at b * cap + r.
-__device__ __forceinline__ void quant_row_fp8(const uint16_t* __restrict__ src, int H, long cap,
-                                              long r, uint8_t* __restrict__ x_perm,
-                                              float* __restrict__ x_scale) {
-    const int nb = H / 128;
-    const int sub = threadIdx.x & 15;
-    for (int b0 = threadIdx.x >> 4; b0 < nb; b0 += 64) {
-        u32x4 q[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int b = b0 + 16 * i;
-            if (b < nb) q[i] = *reinterpret_cast<const u32x4*>(src + b * 128 + sub * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int b = b0 + 16 * i;
-            if (b >= nb) break;
-            const int h0 = b * 128 + sub * 8;
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[2 * e] = bf16_lo(q[i][e]);
-                v[2 * e + 1] = bf16_hi(q[i][e]);
-            }
-            float a = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[e]));
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m));
-            const float sc = block_scale(a);
-            float qv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = clamp_e4m3(v[e] / sc);
-            const uint32_t lo = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3]);
-            const uint32_t hi = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7]);
-            *reinterpret_cast<uint2*>(x_perm + r * H + h0) = make_uint2(lo, hi);
-            if (sub == 0) x_scale[b * cap + r] = sc;
-        }
-    }
-}
-
 // one pass: every used row quantises its token's row (the next row's token
 // index is loaded before this row's work)
 __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
@@ -324,7 +279,7 @@ __global__ __launch_bounds__(256) void perm_gather_fp8_kernel(
     for (; r < used; r += gridDim.x) {
         const long t = token_of(slot, S, k);
         if (r + gridDim.x < used) slot = row_to_slot[r + gridDim.x];
-        quant_row_fp8(x + t * H, H, cap, r, x_perm, x_scale);
+        quant_row_fp8(x + t * H, H, cap, r, x_perm, x_scale, threadIdx.x);
     }
 }
 
@@ -344,7 +299,7 @@ __global__ __launch_bounds__(256) void perm_quant_tokens_fp8_kernel(
     int H, long cap, uint8_t* __restrict__ x_perm, float* __restrict__ x_scale) {
     const long q0 = stage_row0(offsets, E_local, S);
     for (long t = blockIdx.x; t < T; t += gridDim.x)
-        quant_row_fp8(x + t * H, H, cap, q0 + t, x_perm, x_scale);
+        quant_row_fp8(x + t * H, H, cap, q0 + t, x_perm, x_scale, threadIdx.x);
 }
 
 // pass 2: routed row r takes the codes and scales of its token's staging row.
@@ -402,7 +357,7 @@ __global__ __launch_bounds__(256) void perm_copy_fp8_kernel(
 __global__ __launch_bounds__(256) void quant_tokens_fp8_kernel(const uint16_t* __restrict__ x, int T,
                                                                int H, uint8_t* __restrict__ codes,
                                                                float* __restrict__ scales) {
-    for (long t = blockIdx.x; t < T; t += gridDim.x) quant_row_fp8(x + t * H, H, T, t, codes, scales);
+    for (long t = blockIdx.x; t < T; t += gridDim.x) quant_row_fp8(x + t * H, H, T, t, codes, scales, threadIdx.x);
 }
 
 }  // namespace

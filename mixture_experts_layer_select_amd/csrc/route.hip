@@ -15,252 +15,27 @@
 // wave-wide maximum over a 64-bit key (order-preserving logit bits, then the
 // complemented expert index) pick the experts in (logit desc, index asc)
 // order.
-#include "moe_internal.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
 
-constexpr int kWT = 8;        // tokens per wave
-constexpr int kWE = 8;        // experts per wave
-constexpr int kStep = 512;    // h per step: 64 lanes x 8
-
-// 8 consecutive inputs as fp32 (zeros past H)
-template <typename TIn>
-struct Chunk;
-
-template <>
-struct Chunk<uint16_t> {  // bf16 bit patterns: 8 values in one 16-byte load
-    u32x4 raw;
-    __device__ __forceinline__ void load(const uint16_t* row, int h0, int H, bool vec) {
-        if (vec && h0 + 8 <= H) {
-            raw = *reinterpret_cast<const u32x4*>(row + h0);
-        } else {
-            uint32_t v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t lo = h0 + 2 * i < H ? row[h0 + 2 * i] : 0u;
-                uint32_t hi = h0 + 2 * i + 1 < H ? row[h0 + 2 * i + 1] : 0u;
-                v[i] = lo | (hi << 16);
-            }
-            raw = u32x4{v[0], v[1], v[2], v[3]};
-        }
-    }
-    __device__ __forceinline__ float at(int i) const {
-        return (i & 1) ? bf16_hi(raw[i >> 1]) : bf16_lo(raw[i >> 1]);
-    }
-};
-
-template <>
-struct Chunk<float> {
-    f32x4 lo, hi;
-    __device__ __forceinline__ void load(const float* row, int h0, int H, bool vec) {
-        if (vec && h0 + 8 <= H) {
-            lo = *reinterpret_cast<const f32x4*>(row + h0);
-            hi = *reinterpret_cast<const f32x4*>(row + h0 + 4);
-        } else {
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = h0 + i < H ? row[h0 + i] : 0.0f;
-            lo = f32x4{v[0], v[1], v[2], v[3]};
-            hi = f32x4{v[4], v[5], v[6], v[7]};
-        }
-    }
-    __device__ __forceinline__ float at(int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
-};
-
-// A wave owns 8 tokens x 8 experts = 64 (t, e) pairs; a workgroup of 4 waves
-// covers 8 tokens x 32 experts. Lane j reads its 16-byte chunk of each of the
-// 16 rows straight from global memory (a wave reads 1 KB contiguous per row
-// and step), one step ahead in registers; no LDS. Every input row is read
-// whole by every wave that needs it, so reuse happens in L2. Rows past T or E
-// read a valid row; those pairs are never written. Zero padding past H adds
-// fma(0, 0, p) = p exactly (a partial that starts at +0 is never -0).
-// Vector loads need H % 8 == 0 (bf16) / H % 4 == 0 (fp32) for alignment;
-// other H take the element path for every chunk.
 template <typename TIn>
 __global__ __launch_bounds__(256) void route_logits_kernel(const TIn* __restrict__ x,
                                                            const TIn* __restrict__ w,
                                                            const float* __restrict__ bias, int T,
                                                            int H, int E,
                                                            float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kWT;
-    const int e0 = (blockIdx.y * 4 + wave) * kWE;
-    const bool aligned = sizeof(TIn) == 2 ? (H & 7) == 0 : (H & 3) == 0;
-
-    const TIn* xr[kWT];
-    const TIn* wr[kWE];
-#pragma unroll
-    for (int a = 0; a < kWT; ++a) xr[a] = x + (size_t)min(t0 + a, T - 1) * H;
-#pragma unroll
-    for (int b = 0; b < kWE; ++b) wr[b] = w + (size_t)min(e0 + b, E - 1) * H;
-
-    float acc[kWT][kWE];
-#pragma unroll
-    for (int a = 0; a < kWT; ++a)
-#pragma unroll
-        for (int b = 0; b < kWE; ++b) acc[a][b] = 0.0f;
-
-    Chunk<TIn> cx[2][kWT], cw[2][kWE];
-    auto load = [&](int buf, int hs) {
-        const int h0 = hs + 8 * lane;
-#pragma unroll
-        for (int a = 0; a < kWT; ++a) cx[buf][a].load(xr[a], h0, H, aligned);
-#pragma unroll
-        for (int b = 0; b < kWE; ++b) cw[buf][b].load(wr[b], h0, H, aligned);
-    };
-    auto fma_step = [&](int buf) {
-        // partial of lane j, ascending h inside its chunk, every pair
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float xv[kWT], wv[kWE];
-#pragma unroll
-            for (int a = 0; a < kWT; ++a) xv[a] = cx[buf][a].at(i);
-#pragma unroll
-            for (int b = 0; b < kWE; ++b) wv[b] = cw[buf][b].at(i);
-#pragma unroll
-            for (int a = 0; a < kWT; ++a)
-#pragma unroll
-                for (int b = 0; b < kWE; ++b) acc[a][b] = __builtin_fmaf(xv[a], wv[b], acc[a][b]);
-        }
-    };
-    load(0, 0);
-    int hs = 0;
-    for (;;) {
-        const bool more = hs + kStep < H;
-        if (more) load(1, hs + kStep);
-        __builtin_amdgcn_sched_barrier(0);
-        fma_step(0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!more) break;
-        hs += kStep;
-        const bool more2 = hs + kStep < H;
-        if (more2) load(0, hs + kStep);
-        __builtin_amdgcn_sched_barrier(0);
-        fma_step(1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!more2) break;
-        hs += kStep;
-    }
-
-    // transposing pairwise reduction: pair p = a*8 + b ends in lane p
-    float v[64];
-#pragma unroll
-    for (int a = 0; a < kWT; ++a)
-#pragma unroll
-        for (int b = 0; b < kWE; ++b) v[a * kWE + b] = acc[a][b];
-#pragma unroll
-    for (int s = 32, n = 64; s >= 1; s >>= 1, n >>= 1) {
-        const bool hi = (lane & s) != 0;
-#pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-            float keep = hi ? v[n / 2 + i] : v[i];
-            float give = hi ? v[i] : v[n / 2 + i];
-            float got = __shfl_xor(give, s);
-            v[i] = keep + got;
-        }
-    }
-    const int t = t0 + (lane >> 3);
-    const int e = e0 + (lane & 7);
-    if (t < T && e < E) {
-        float l = v[0];
-        if (bias) l = l + bias[e];
-        logits[(size_t)t * E + e] = l;
-    }
+    route_logits_tile(x, w, bias, T, H, E, logits, blockIdx.x * kWT, (blockIdx.y * 4 + wave) * kWE);
 }
 
-__device__ __forceinline__ uint32_t ordered_bits(float l) {
-    uint32_t u = (l == 0.0f) ? 0u : __float_as_uint(l);  // -0 ties with +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float from_ordered(uint32_t o) {
-    uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
-    return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, s);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), s);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
-    return v;
-}
-
-// one wave per token; E <= 256, k <= E
+// one wave per token
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int scoring, int renorm,
                                                          int32_t* __restrict__ ids,
                                                          float* __restrict__ topk_w) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float* l = logits + (size_t)t * E;
-    uint64_t key[4];
-    float lv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int e = lane + 64 * i;
-        lv[i] = e < E ? l[e] : 0.0f;
-        key[i] = e < E ? (((uint64_t)ordered_bits(lv[i]) << 32) | (0xffffffffu - (uint32_t)e)) : 0;
-    }
-    int my_id[4] = {0, 0, 0, 0};
-    float my_l[4] = {0.f, 0.f, 0.f, 0.f};
-    float lmax = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(0xffffffffu - (uint32_t)best);
-        const float lb = from_ordered((uint32_t)(best >> 32));
-        if (j == 0) lmax = lb;
-        if ((e & 63) == lane) key[e >> 6] = 0;  // taken
-        if ((j & 63) == lane) {
-            my_id[j >> 6] = e;
-            my_l[j >> 6] = lb;
-        }
-    }
-    // weights
-    float num[4], part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bool mine = lane + 64 * i < k;
-        float v;
-        if (scoring == MOE_SIGMOID) v = 1.0f / (1.0f + expf(-my_l[i]));
-        else v = expf(my_l[i] - lmax);
-        num[i] = mine ? v : 0.0f;
-        part += num[i];
-    }
-    float den;
-    if (renorm) {
-        den = wave_sum(part);
-    } else if (scoring == MOE_SOFTMAX) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i < E) s += expf(lv[i] - lmax);
-        den = wave_sum(s);
-    } else {
-        den = 1.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = lane + 64 * i;
-        if (j < k) {
-            ids[(size_t)t * k + j] = my_id[i];
-            topk_w[(size_t)t * k + j] = num[i] / den;
-        }
-    }
+    route_topk_token(logits, T, E, k, scoring, renorm, ids, topk_w, blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------- candidate routing

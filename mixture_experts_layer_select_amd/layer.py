@@ -196,6 +196,32 @@ class MoELayer:
                 if tuple(t.shape) != (x.shape[0], self.k):
                     raise ValueError(f"{name}: shape {tuple(t.shape)}, expected [{x.shape[0]}, {self.k}]")
 
+    # the one-launch layer (moe_layer_fused) takes batches up to this size
+    FUSED_MAX_T = 256
+
+    def fused_workspace(self, T: int) -> torch.Tensor:
+        """The fused layer's workspace for T tokens, zeroed once at allocation
+        (its barrier words must start at zero; every call leaves them so)."""
+        key = ("fused", T)
+        if key not in self._bufs:
+            E = self.router["w"].shape[0]
+            n = L.moe_layer_fused_workspace_size(self.weights, T, E, self.k)
+            self._bufs[key] = torch.zeros(max(n, 256), dtype=torch.uint8, device=self.w13.device)
+        return self._bufs[key]
+
+    def forward_fused(self, x: torch.Tensor, stream=None) -> LayerBuffers:
+        """The whole layer in one launch (routing by this layer's router, all
+        experts local): the same ids, weights and output as forward()."""
+        self.check_inputs(x)
+        T = x.shape[0]
+        b = self.buffers(T, x.device)
+        ws = self.fused_workspace(T)
+        r = self.router
+        L.moe_layer_fused(x, r["w"], r.get("bias"), T, r["w"].shape[0], self.k, r["scoring"],
+                          r.get("renormalize", True), self.weights, b.topk_ids, b.topk_w, b.out, ws,
+                          ws.numel(), stream)
+        return b
+
     def forward(self, x: torch.Tensor, topk_ids=None, topk_w=None, stream=None) -> LayerBuffers:
         """The whole layer. Routing comes from the router unless given."""
         self.check_inputs(x, topk_ids, topk_w)

@@ -235,3 +235,27 @@ def test_noalloc_ffn_refuses_rows_beyond_its_static_scratch():
     st = lib.moe_expert_ffn_noalloc(C.byref(w), None, None, None, E, big, None, None)
     assert lib.moe_status_string(st).decode() == "MOE_ERR_WORKSPACE"
     assert b"static array" in lib.moe_last_error_message()
+
+
+def test_fused_layer_rejects_what_it_does_not_cover():
+    """moe_layer_fused checks its limits before anything is enqueued (no
+    device call is made here)."""
+    import torch
+    import mixture_experts_layer_select_amd as L
+    H, I, E = 512, 256, 8
+    w = L.make_weights(L.BF16, E, H, I, torch.zeros((E, 2 * I, H), dtype=torch.bfloat16),
+                       torch.zeros((E, H, I), dtype=torch.bfloat16))
+    lib = L.lib()
+    def call(T, E_, k, ws_bytes=1 << 30):
+        return lib.moe_status_string(lib.moe_layer_fused(
+            None, None, None, T, E_, k, L.SIGMOID, 1, C.byref(w), None, None, None, None, ws_bytes,
+            None)).decode()
+    assert call(257, E, 4) == "MOE_ERR_UNSUPPORTED"      # more than 256 tokens
+    assert call(16, E, 9) == "MOE_ERR_INVALID_ARG"       # k > E
+    assert call(16, 16, 4) == "MOE_ERR_INVALID_ARG"      # experts not all local (E_local 8)
+    assert call(16, E, 8) == "MOE_ERR_INVALID_ARG"       # null pointers (k = 8 is covered)
+    assert call(16, 16, 9) == "MOE_ERR_UNSUPPORTED"      # k > 8
+    assert call(16, E, 0) == "MOE_ERR_INVALID_ARG"
+    assert call(0, E, 4) == "MOE_OK"                     # nothing to do
+    assert call(16, E, 4) == "MOE_ERR_INVALID_ARG"       # null pointers
+    assert L.moe_layer_fused_workspace_size(w, 16, E, 4) > 256
