@@ -20,8 +20,11 @@
 // Grid barrier: an arrival counter and a generation word in the workspace.
 // The last workgroup to arrive resets the counter and bumps the generation;
 // the others poll the generation with a sleep between polls, for a bounded
-// number of polls. Agent-scope release before arriving and acquire after
-// leaving make each phase's global writes visible to every XCD. The grid is
+// number of polls. Agent-scope release before arriving (the L2 write-back of
+// this XCD) and acquire after leaving (the invalidation of this CU's vector
+// cache and of its XCD's L2), each by one thread of the workgroup after a
+// workgroup barrier, make each phase's global writes visible to every XCD.
+// The grid is
 // one workgroup per CU, all resident at once on an otherwise idle device; if
 // a poll limit is reached (the grid was not resident), the error word is set,
 // the waves carry on, and the outputs are invalid.
@@ -61,9 +64,12 @@ __device__ __forceinline__ void grid_sync(GridBar* b) {
                 __builtin_amdgcn_s_sleep(2);
             }
         }
+        // one acquire per workgroup: the invalidation it issues covers this
+        // CU's vector cache and its XCD's L2, which every wave here reads
+        // through (one per wave tripled the barrier's cost)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 struct FusedArgs {
