@@ -58,7 +58,10 @@ def parse():
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--fused-T", default="1,16,64,256",
                     help="batch sizes at which the one-launch layer (moe_layer_fused) is timed against "
-                         "the five-launch path on the same weights ('' = skip)")
+                         "the five-launch path on the same weights ('none' = skip)")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="only the small-batch comparison on the --config layer (for kernel traces); "
+                         "prints its JSON record instead of the benchmark line")
     ap.add_argument("--graph", action="store_true",
                     help="after the eager timed steps, capture one step in a HIP graph and also "
                          "report the replay time (graph_ms_per_step)")
@@ -191,14 +194,23 @@ def layer_alg(cfg, layer, counts, T, n_rows):
     return byt, flops
 
 
+def gemm_source_digest() -> str:
+    """SHA-256 over the sources of the grouped GEMM kernels (device code, then
+    kernels and launchers): a committed counter summary applies only to them."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("ffn_dev.h", "ffn.hip"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_layer_select_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def profiled_traffic(kernel_key: str, workload: str):
     """HBM bytes per launch from the committed counter summary of this kernel
     and workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
     size), or None when there is none or the kernel source changed since."""
     import glob
     import hashlib
-    src = os.path.join(ROOT, "mixture_experts_layer_select_amd", "csrc", "ffn.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = gemm_source_digest()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(path):
             line = line.strip()
@@ -209,7 +221,7 @@ def profiled_traffic(kernel_key: str, workload: str):
             except ValueError:
                 continue
             if (rec.get("kernel") == kernel_key and rec.get("workload") == workload
-                    and rec.get("ffn_hip_sha256") == digest):
+                    and rec.get("gemm_sources_sha256") == digest):
                 return int(rec["traffic_bytes"])
     return None
 
@@ -457,7 +469,7 @@ def measure(cid: int, args, dev: str, with_cpu: bool) -> dict:
                       "affinity_partition_host_ms": round(part_ms, 3),
                       "partition": f"E={cfg.E} into {G} sets, load cap +2%"},
     }
-    Ts = [int(t) for t in args.fused_T.split(",") if t.strip()]
+    Ts = [int(t) for t in args.fused_T.split(",") if t.strip() and t.strip() != "none"]
     if Ts and layer.router is not None and layer.E_local == cfg.E and cfg.k <= 8:
         line["fused_small_batch"] = {"layer": f"c{cfg.cid} weights, {cfg.fmt}",
                                      **fused_sweep(cfg, layer, Ts, dev)}
@@ -482,6 +494,12 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.fused_only:
+        cfg, layer, x, st, sh, topk, info = build_layer(args.config, dev)
+        Ts = [int(t) for t in args.fused_T.split(",") if t.strip() and t.strip() != "none"]
+        print(json.dumps({"fused_small_batch": {"layer": f"c{cfg.cid} weights, {cfg.fmt}",
+                                                **fused_sweep(cfg, layer, Ts, dev)}}), flush=True)
+        return
     line = measure(args.config, args, dev, with_cpu=True)
     if args.decode_config and args.decode_config != args.config:
         gc.collect()
