@@ -37,6 +37,7 @@ namespace moe {
 namespace {
 
 constexpr int kFusedThreads = 512;
+constexpr int kFusedRowsMaxT = 64;  // batches routed one (token, expert) pair per wave
 constexpr unsigned kPollLimit = 1u << 20;  // polls before a barrier gives up (about a second)
 
 struct GridBar {
@@ -114,8 +115,12 @@ __global__ __launch_bounds__(kFusedThreads) void moe_layer_fused_kernel(FusedArg
     const int gw = blockIdx.x * (kFusedThreads / 64) + wave;  // wave index in the grid
     const int nw = gridDim.x * (kFusedThreads / 64);
 
-    // 1. router logits
-    {
+    // 1. router logits: one (token, expert) pair per wave for small batches,
+    // 8 x 8 tiles otherwise (the same logits bit for bit)
+    if (p.T <= kFusedRowsMaxT && p.H <= 16 * kStep) {
+        for (int q = gw; q < p.T * p.E; q += nw)
+            route_logits_row<16>(p.x, p.wr, p.bias, p.H, p.E, p.logits, q / p.E, q % p.E);
+    } else {
         const int n_et = (p.E + kWE - 1) / kWE;
         const int tasks = (p.T + kWT - 1) / kWT * n_et;
         for (int q = gw; q < tasks; q += nw)

@@ -155,6 +155,46 @@ __device__ __forceinline__ void route_logits_tile(const TIn* __restrict__ x, con
     }
 }
 
+// Small batches: one wave computes one (token, expert) logit with both rows
+// read whole into registers up front (kSteps chunks of 16 bytes per lane and
+// row), so it waits for one memory latency instead of one per 512-element
+// step. Lane j runs the same fma chain over its chunks as route_logits_tile,
+// and the butterfly below adds the 64 partials over lane bits 5..0 in the
+// same tree as its transposing reduction (each level adds the same two
+// values; fp32 addition commutes), so the logit is bit-identical. Rows are
+// read through descriptors of the row's size: chunks past H read zeros
+// (H % 8 == 0, so a chunk is either inside the row or past it) and the steps
+// past ceil(H/512) are skipped. Needs H <= kSteps * 512.
+template <int kSteps>
+__device__ __forceinline__ void route_logits_row(const uint16_t* __restrict__ x,
+                                                 const uint16_t* __restrict__ w,
+                                                 const float* __restrict__ bias, int H, int E,
+                                                 float* __restrict__ logits, int t, int e) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t row_bytes = (uint32_t)H * 2u;
+    const __amdgpu_buffer_rsrc_t wd = buffer_rsrc(w + (size_t)e * H, row_bytes);
+    const __amdgpu_buffer_rsrc_t xd = buffer_rsrc(x + (size_t)t * H, row_bytes);
+    u32x4 wc[kSteps], xc[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) wc[s] = buffer_load16(wd, (uint32_t)(512 * s + 8 * lane) * 2u, 0);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) xc[s] = buffer_load16(xd, (uint32_t)(512 * s + 8 * lane) * 2u, 0);
+    const int nsteps = (H + kStep - 1) / kStep;
+    float p = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+        if (s < nsteps) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                p = __builtin_fmaf(bf16_lo(xc[s][q]), bf16_lo(wc[s][q]), p);
+                p = __builtin_fmaf(bf16_hi(xc[s][q]), bf16_hi(wc[s][q]), p);
+            }
+        }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s);
+    if (lane == 0) logits[(size_t)t * E + e] = bias ? p + bias[e] : p;
+}
+
 __device__ __forceinline__ uint32_t ordered_bits(float l) {
     uint32_t u = (l == 0.0f) ? 0u : __float_as_uint(l);  // -0 ties with +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

@@ -91,3 +91,44 @@ def test_route_large_batch_sampled():
     rows = np.sort(np.random.default_rng(0).choice(cfg.T, 384, replace=False))
     _check(x, mi.router_weight(cfg, device=DEV), mi.router_bias(cfg, device=DEV), cfg.k,
            oracle.SIGMOID, True, rows=rows)
+
+
+# Batches of up to 32 bf16 tokens (H % 8 == 0, H <= 8192) take the row
+# kernels: one wave per expert and one or two tokens, the whole rows in
+# registers. Same fixed-order logits bit for bit.
+@pytest.mark.parametrize("T,H,E,k", [
+    (1, 7168, 256, 8), (2, 7168, 256, 8), (3, 7168, 256, 8), (4, 7168, 256, 8),
+    (5, 7168, 256, 8), (16, 7168, 256, 8), (31, 7168, 256, 8), (32, 7168, 256, 8),
+    (7, 8192, 64, 6),     # 16 steps, all with data
+    (9, 4104, 36, 4),     # 9 steps, the last one ragged; E not a multiple of 4
+    (2, 520, 3, 2),       # 2 steps; fewer experts than a workgroup's waves
+])
+def test_route_small_batch_rows(T, H, E, k):
+    cfg = mi.scaled(mi.CONFIGS[2], T=T, H=H, E=E, zipf_s=1.1)
+    _check(mi.tokens(cfg, device=DEV), mi.router_weight(cfg, device=DEV),
+           mi.router_bias(cfg, device=DEV), k, oracle.SIGMOID, True)
+
+
+def test_route_small_batch_rows_match_tile_kernel_on_extreme_values():
+    # 32 tokens take the row kernel, 40 the 8 x 8 tile kernel: the first 32
+    # tokens' logits must agree bit for bit, also with denormal inputs, huge
+    # rows and exact zeros, where the oracle's numpy arithmetic might not flush
+    # the way the GPU does
+    cfg = mi.scaled(mi.CONFIGS[2], T=40, H=7168, E=256, zipf_s=1.1)
+    x = mi.tokens(cfg, device=DEV)
+    wr = mi.router_weight(cfg, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    tiny = torch.full((40, 7168), 1e-39, dtype=torch.float32)
+    mask = torch.rand((40, 7168), generator=g) < 0.1
+    x = torch.where(mask.to(DEV), tiny.to(DEV), x.float()).to(torch.bfloat16)
+    x[3] = 0.0
+    x[4, 100:] = 0.0
+    wr = wr.clone()
+    wr[::16] *= 1000.0
+    wr[7] = (wr[7].float() * 1e-38).to(torch.bfloat16)
+    b = mi.router_bias(cfg, device=DEV)
+    l40, i40, w40 = _route_gpu(x, wr, b, 8, oracle.SIGMOID, True)
+    l32, i32, w32 = _route_gpu(x[:32].contiguous(), wr, b, 8, oracle.SIGMOID, True)
+    assert np.array_equal(l32.view(np.uint32), l40[:32].view(np.uint32))
+    assert np.array_equal(i32, i40[:32])
+    assert np.array_equal(w32.view(np.uint32), w40[:32].view(np.uint32))
