@@ -531,7 +531,7 @@ moe_status launch_ffn_gate_up(const moe_expert_weights* w, const void* x_perm,
                                w->w13_scale, (const uint8_t*)w->ws13, w->ws13_scale, E, offsets,
                                n_groups, max_rows, H, 2 * I, NB, s.a, s.a_scale, I, src);
         moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<gate_up>");
-        if (r) return r;
+        if (r || max_rows <= kLTM) return r;  // no group can exceed the buffer's rows
         const long tl = 2L * max_rows / kGTM + 1;  // tiles of groups above 256 rows
         if (src.row_slot)
             hipLaunchKernelGGL((ffn_gemm_fp8_big_kernel<true, true>), dim3(persistent_grid_xcd(tl * NB, 1)),
@@ -585,7 +585,7 @@ moe_status launch_ffn_down(const moe_expert_weights* w, const int32_t* offsets, 
                            w->w2_scale, (const uint8_t*)w->ws2, w->ws2_scale, E, offsets, n_groups,
                            max_rows, I, H, NB, y_perm, nullptr, H, ActSrc{nullptr, 0, 0, 0, 0});
         moe_status r = check_launch("ffn_gemm_fp8_lds_kernel<down>");
-        if (r) return r;
+        if (r || max_rows <= kLTM) return r;
         const long tl = 2L * max_rows / kGTM + 1;
         hipLaunchKernelGGL((ffn_gemm_fp8_big_kernel<false, false>), dim3(persistent_grid_xcd(tl * NB, 1)),
                            dim3(kLThreads), 0, st, (const uint8_t*)s.a, s.a_scale, (const uint8_t*)w->w2,

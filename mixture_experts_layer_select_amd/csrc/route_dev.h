@@ -204,15 +204,32 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
     return __uint_as_float(u);
 }
 
+// The maximum of v over the wave's 64 lanes. Each row of 16 lanes by DPP
+// moves (partners lane ^ 1, lane ^ 2, then the mirrored half-rows and rows),
+// which leaves the row's maximum in all of its lanes; then the four row
+// maxima are read into scalar registers. No LDS round trips; the result is
+// wave-uniform. (Integer keys: any order of comparisons gives the same max.)
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, 0xf, 0xf, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = dpp_max_u64<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+    v = dpp_max_u64<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+    v = dpp_max_u64<0x141>(v);  // row_half_mirror: lane i <-> 7 - i in each half-row
+    v = dpp_max_u64<0x140>(v);  // row_mirror: lane i <-> 15 - i in each row
+    uint64_t m = 0;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, s);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), s);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        m = o > m ? o : m;
     }
-    return v;
+    return m;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
