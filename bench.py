@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--decode-config", type=int, default=2, choices=[0, 2, 3, 5],
                     help="second workload timed in the same process after the first and "
                          "reported under 'decode' (0 = none)")
+    ap.add_argument("--also-configs", default="3,5",
+                    help="further workloads timed in the same process after the first two and "
+                         "reported under 'also' (comma list of 3 and 5; 'none' = skip)")
     ap.add_argument("--cpu-sample", type=int, default=256,
                     help="tokens of the workload the CPU oracle runs end to end (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -483,6 +486,14 @@ def measure(cid: int, args, dev: str, with_cpu: bool) -> dict:
     return line
 
 
+def dict_args(args, **changes):
+    """A copy of the parsed arguments with some fields replaced."""
+    a = argparse.Namespace(**vars(args))
+    for key, v in changes.items():
+        setattr(a, key, v)
+    return a
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -508,6 +519,16 @@ def main():
         line["decode"] = {key: d[key] for key in ("value", "unit", "ms_per_step", "dtype", "config",
                                                   "roofline", "layer_roofline", "fused_small_batch")
                           if key in d}
+    also = [int(c) for c in args.also_configs.split(",") if c.strip() and c.strip() != "none"]
+    for cid in also:
+        if cid in (args.config, args.decode_config) or cid not in (2, 3, 5):
+            continue
+        gc.collect()
+        torch.cuda.empty_cache()
+        a = measure(cid, dict_args(args, fused_T="none"), dev, with_cpu=False)
+        line.setdefault("also", {})[a["config"]["workload"]] = {
+            key: a[key] for key in ("value", "unit", "ms_per_step", "dtype", "config", "roofline",
+                                    "layer_roofline") if key in a}
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
