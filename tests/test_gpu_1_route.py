@@ -93,12 +93,13 @@ def test_route_large_batch_sampled():
            oracle.SIGMOID, True, rows=rows)
 
 
-# Batches of up to 32 bf16 tokens (H % 8 == 0, H <= 8192) take the row
+# Batches of up to 64 bf16 tokens (H % 8 == 0, H <= 8192) take the row
 # kernels: one wave per expert and one or two tokens, the whole rows in
 # registers. Same fixed-order logits bit for bit.
 @pytest.mark.parametrize("T,H,E,k", [
     (1, 7168, 256, 8), (2, 7168, 256, 8), (3, 7168, 256, 8), (4, 7168, 256, 8),
     (5, 7168, 256, 8), (16, 7168, 256, 8), (31, 7168, 256, 8), (32, 7168, 256, 8),
+    (64, 7168, 256, 8), (65, 7168, 256, 8),  # the last row-kernel batch, the first tile one
     (7, 8192, 64, 6),     # 16 steps, all with data
     (9, 4104, 36, 4),     # 9 steps, the last one ragged; E not a multiple of 4
     (2, 520, 3, 2),       # 2 steps; fewer experts than a workgroup's waves
