@@ -2,8 +2,9 @@
 (moe_layer_fused; Moreh EP report, Library optimization: a fused MoE kernel
 for small batch sizes; Use of HIP Graphs). On the R1 decode shape (H = 7168,
 256 routed experts of intermediate 2048, top-8 by sigmoid score with the
-Zipf-skewed router, one shared expert), in bf16 and fp8, at T = 1, 16, 64 and
-256 tokens: routing ids and weights, and the output, bit for bit those of the
+Zipf-skewed router, one shared expert), in bf16 and fp8, at T = 1, 16, 37, 64,
+65, 129 and 256 tokens (ragged batches on both sides of the router's row/tile
+switch at 64): routing ids and weights, and the output, bit for bit those of the
 separate calls (route, permute, expert FFN, combine); the output against the
 oracle on every token; the barrier words back at zero; graph replays equal to
 eager calls."""
@@ -45,7 +46,7 @@ def _barrier_words(layer, T):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("T", [1, 16, 64, 256])
+@pytest.mark.parametrize("T", [1, 16, 37, 64, 65, 129, 256])
 def test_fused_layer_matches_separate_calls_and_oracle(r1_layer, T):
     fmt, cfg, layer, st, sh = r1_layer
     x = mi.tokens(cfg, T=T, device=DEV, tensor=20)
