@@ -4,8 +4,8 @@
 //
 // One workgroup of 512 threads per CU runs the layer's steps as phases, with
 // a grid-wide barrier between them:
-//   1. router logits (8 x 8 token-expert tiles, one per wave, the fixed fp32
-//      order of moe_route)                                    barrier
+//   1. router logits (one token-expert pair per wave up to 64 tokens, else
+//      8 x 8 tiles per wave; the fixed fp32 order of moe_route) barrier
 //   2. top-k and combine weights (one wave per token)          barrier
 //   3. the permutation in workgroup 0; fp8: every token quantised once (1x128
 //      blocks) by the other workgroups                       barrier
