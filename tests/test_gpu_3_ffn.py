@@ -172,3 +172,54 @@ def test_ffn_every_group_empty(fmt):
     L.moe_expert_ffn(w, xp, xs, off, E_local, max_rows, y, ws, ws_n)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("rows", [1, 5, 8, 9, 16])
+def test_ffn_fp8_small_group_rows_do_not_depend_on_the_group_height(rows):
+    """A row's result does not depend on how many rows its group has: two
+    experts with the same weights, the first given `rows` rows (one 16-token
+    block, one or two 8-row staging pieces) and the second the same rows plus
+    more (17 or more rows: two blocks): gate/up codes and scales and the down
+    output of those rows agree bit for bit, at the R1 shape."""
+    import mixture_experts_layer_select_amd as L
+    cfg = mi.CONFIGS[4]
+    H, I = cfg.H, cfg.I
+    st = mi.stacked_expert_weights(cfg, [3], device=DEV)
+    w13 = st["w13"].repeat(2, 1, 1).contiguous()
+    w2 = st["w2"].repeat(2, 1, 1).contiguous()
+    s13 = st["w13_scale"].repeat(2, 1, 1).contiguous()
+    s2 = st["w2_scale"].repeat(2, 1, 1).contiguous()
+    w = L.make_weights(L.FP8_E4M3, 2, H, I, w13, w2, s13, s2)
+    n2 = max(rows + 1, 17)
+    x = mi.normal((n2, H), 1.0, 4242 + rows, DEV, torch.bfloat16)
+    codes, scales = oracle.quantize_1x128(x.float().cpu().numpy())
+    xc = torch.from_numpy(codes).to(DEV)
+    xs = torch.from_numpy(scales).to(DEV)                       # [n2][H/128]
+    R = rows + n2
+    max_rows = R + 3
+    xp = torch.zeros((max_rows, H), dtype=torch.uint8, device=DEV)
+    xp[:rows] = xc[:rows]
+    xp[rows:R] = xc
+    xps = torch.ones((H // 128, max_rows), dtype=torch.float32, device=DEV)
+    xps[:, :rows] = xs[:rows].t()
+    xps[:, rows:R] = xs.t()
+    off = torch.tensor([0, rows, R], dtype=torch.int32, device=DEV)
+    ws_n = L.moe_expert_ffn_workspace_size(w, max_rows)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=DEV)
+    y = torch.zeros((max_rows, H), dtype=torch.bfloat16, device=DEV)
+    L.moe_expert_ffn(w, xp, xps, off, 2, max_rows, y, ws, ws_n)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:rows].view(torch.int16), y[rows:2 * rows].view(torch.int16))
+    # the intermediate: codes [max_rows][I] at the start of the workspace,
+    # then its scales [I/128][max_rows]
+    a = ws[:max_rows * I].view(max_rows, I)
+    a_off = ((max_rows * I + 255) // 256) * 256
+    a_sc = ws[a_off:a_off + max_rows * (I // 128) * 4].view(torch.float32).view(I // 128, max_rows)
+    assert torch.equal(a[:rows], a[rows:2 * rows])
+    assert torch.equal(a_sc[:, :rows].view(torch.int32), a_sc[:, rows:2 * rows].view(torch.int32))
+    groups = [cpu_expert(st, 0), cpu_expert(st, 0)]
+    ref = oracle.expert_ffn(groups, xp[:R].cpu(), xps[:, :R].t().contiguous().cpu(),
+                            off.cpu().numpy(), H, I)
+    e = rel_err(y[:R].float().cpu().numpy(), ref)
+    say(f"  group of {rows} rows: bit-identical to the {n2}-row group, vs oracle {e:.3e}")
+    assert e <= TOL["fp8"]
